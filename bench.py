@@ -1,0 +1,233 @@
+"""Throughput of the quantized expert FFN decode layer on one MI355X.
+
+Default workload: routed MoE expert FFN decode layer with hidden 6144, 320
+experts, intermediate 2048, top-8 routing, one token, int4-g64 gate/up/down,
+bf16 activations.  One step = one moe_expert_ffn layer call (gate+up+SiLU,
+down, weighted combine) over a fresh routing draw.  Routing draws walk
+through random permutations of the 320 experts so that an expert's weights
+are re-read only after all others (6.8 GB later), far past the 256 MB
+last-level cache: every step streams its 8 experts from HBM.
+
+Prints one JSON line:  value = algorithmic bytes per step (routed experts'
+weights + scales, each read once, plus x and y) / time per step, in GB/s.
+`roofline` reports the dominant kernel (fused gate+up+SiLU, about two thirds
+of the bytes), timed with HIP events recorded on the launch stream around
+its launches inside the timed region.  `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same steps.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s + µs/layer for int4-g64 MoE expert FFN decode (B=1)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "gemv"])
+    p.add_argument("--tokens", type=int, default=1)
+    p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
+    p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
+    p.add_argument("--n", type=int, default=6144)
+    p.add_argument("--k", type=int, default=6144)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def expert_bytes(fmt, H, I, gs):
+    """Weights + scales of one expert (gate, up, down), as stored."""
+    if fmt == 4:
+        gh = 1 if not gs else H // gs
+        gi = 1 if not gs else I // gs
+        return 2 * I * (H // 2 + 4 * gh) + H * (I // 2 + 4 * gi)
+    return 2 * I * (H + 4) + H * (I + 4)
+
+
+def routing_schedule(seed, n_steps, T, E, k):
+    """Per step: T tokens' top-k ids (distinct within a token) taken from a
+    walk over random permutations of the experts, and softmax gate weights."""
+    g = np.random.default_rng([seed, 1234])
+    need = n_steps * T * k
+    perm = np.concatenate([g.permutation(E) for _ in range(need // E + 2)])
+    ids = perm[:need].reshape(n_steps, T, k).astype(np.int32)
+    logits = g.standard_normal(size=(n_steps, T, k))
+    w = np.exp(logits - logits.max(axis=2, keepdims=True))
+    w = (w / w.sum(axis=2, keepdims=True)).astype(np.float32)
+    return ids, w
+
+
+def bench_moe(args, E, H, I):
+    import torch
+    from int4_expert_gemv_amd import qmoe, synth
+    from oracle import ref
+
+    T, k, gs, fmt = args.tokens, 8, args.gs, 4
+    n_steps = args.warmup + args.steps
+    print("generating %d experts (hidden %d, inter %d, int4 gs=%d)" % (E, H, I, gs), file=sys.stderr, flush=True)
+    t0 = time.time()
+    ex = synth.expert_set(args.seed, fmt, E, H, I, gs, threads=min(16, os.cpu_count() or 4))
+    d = {key: dev(ex[key]) for key in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}
+    torch.cuda.synchronize()
+    print("generated+uploaded in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
+    e = qmoe.experts(fmt, gs, d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
+    ids_h, w_h = routing_schedule(args.seed, n_steps, T, E, k)
+    x_h = synth.activations(np.random.default_rng([args.seed, 5]), (n_steps, T, H), "bf16")
+    ids_d, w_d, x_d = dev(ids_h), dev(w_h), dev(x_h)
+    ws = torch.empty(qmoe.moe_expert_ffn_workspace(e, T, k), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T * k, I), dtype=torch.float32, device="cuda")
+    y = torch.empty((n_steps, T, H), dtype=torch.float32, device="cuda")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        qmoe.moe_gate_up(e, x_d[i], ids_d[i], h)
+        if ev is not None:
+            ev[1].record()
+        qmoe.moe_down(e, h, ids_d[i], w_d[i], y[i], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # the fused moe_expert_ffn entry point on the same steps, untimed, must agree bit for bit
+    y2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    last = n_steps - 1
+    qmoe.moe_expert_ffn(e, x_d[last], ids_d[last], w_d[last], y2, ws)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y2, y[last]))
+
+    # parity of the last step against the oracle
+    o = ref.oracle()
+    yr, _, nr = o.moe_ffn(ex, x_h[last], ids_h[last], w_h[last])
+    err = ref.max_norm_err(y[last].cpu().numpy(), yr, nr)
+
+    ebytes = expert_bytes(fmt, H, I, gs)
+    uniq = [len(np.unique(ids_h[args.warmup + j])) for j in range(args.steps)]
+    step_bytes = float(np.mean(uniq)) * ebytes + T * H * 2 + T * H * 4 + T * k * 8
+    gu_bytes = float(np.mean(uniq)) * (2 * I * (H // 2 + 4 * (H // gs if gs else 1))) + T * H * 2
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        threads = len(os.sched_getaffinity(0))
+        o.set_threads(threads)
+        t0 = time.time()
+        done = 0
+        while done < n_steps and (time.time() - t0) < args.cpu_seconds:
+            o.moe_ffn(ex, x_h[done], ids_h[done], w_h[done], want_norm=False)
+            done += 1
+        el = time.time() - t0
+        cpu = {"value": round(done * step_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": "%d of the same decode steps (routing draws 0..%d), fp64 oracle, OpenMP over rows; "
+                         "%.2f ms per step" % (done, done - 1, 1e3 * el / max(done, 1))}
+
+    gname = "g%d" % gs if gs else "row"
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_layer": round(ms_step * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, top-%d, %d token(s), "
+                               "int4-%s weights, bf16 x" % (H, E, I, k, T, gname),
+                   "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": "int4-" + gname,
+                   "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_gate_up_kernel (fused gate+up+SiLU)", "us_per_launch": round(gu_ms * 1e3, 3),
+                     "bytes_per_launch": int(gu_bytes)},
+        "parity": {"max_norm_err": err, "tol": 2e-4, "fused_entry_point_identical": same},
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_gemv(args):
+    import torch
+    from int4_expert_gemv_amd import qmoe, synth
+    from oracle import ref
+
+    fmt, n, k, gs = args.fmt, args.n, args.k, (args.gs if args.fmt == 4 else 0)
+    mb = (n * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else n * (k + 4)
+    copies = max(1, -(-(1 << 30) // mb))  # at least 1 GiB of distinct weights in rotation
+    g = np.random.default_rng([args.seed, 77])
+    qw, s = synth.quant_matrix(g, fmt, n, k, gs)
+    mats = []
+    for c in range(copies):
+        mats.append(qmoe.qmat(fmt, dev(qw), dev(s), n, k, gs))
+    x_h = synth.activations(g, (k,), "bf16")
+    x = dev(x_h)
+    y = torch.empty(n, device="cuda")
+    for i in range(args.warmup):
+        qmoe.qgemv(mats[i % copies], x, y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for j in range(args.steps):
+        qmoe.qgemv(mats[j % copies], x, y)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    yr, nr = ref.oracle().gemv(fmt, n, k, gs, qw, s, x_h)
+    err = ref.max_norm_err(y.cpu().numpy(), yr, nr)
+    byts = mb + k * 2 + n * 4
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"metric": "achieved HBM GB/s for quantized GEMV", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "qgemv %dx%d %s, bf16 x, %d weight copies in rotation" %
+                                   (n, k, ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else "int8-row",
+                                    copies)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in the design "
+              "notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.config == "moe_large":
+        out = bench_moe(args, 320, 6144, 2048)
+    elif args.config == "moe_35b":
+        out = bench_moe(args, 256, 2048, 512)
+    else:
+        out = bench_gemv(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

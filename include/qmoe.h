@@ -1,0 +1,174 @@
+/*
+ * qmoe.h -- C ABI of libqmoe.so: int4/int8 quantized GEMV, small-batch GEMV
+ * and the routed MoE expert FFN on an MI355X (gfx950) GPU.
+ *
+ * Sources (colibri pull-request pages):
+ *  [V] "Vulkan backend: expert tier + dense + MLA attention on any Vulkan 1.2
+ *      GPU (successor to #84)" -- commit notes "backend_vulkan.c/.h +
+ *      shaders/qmatmul.comp" (int4 nibble-8 and int8 per-row GEMV with an
+ *      S-token batch), "qmatmul_gate_up.comp" (fused silu(gate x) * up x),
+ *      the K-expert group note (gate_up for K experts, one barrier, down,
+ *      hidden kept on the device), "fmt=4 grouped scales" (one scale per gs
+ *      inputs of a row), and the PR summary (batch-union prefill touches
+ *      nearly every expert; a cooperative-matrix prefill is future work).
+ *  [Q] "qwen36: Vulkan expert tier, and staged device-local uploads" --
+ *      int4-gs64 as fmt 4 / group 64, int8 experts as fmt 1, and the
+ *      issue/take path accumulating expert outputs with their routing weights.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked "device" are HIP device pointers; the caller owns every
+ *    buffer (weights, activations, outputs, workspace).  The library keeps no
+ *    pointer after a call returns, allocates nothing and holds no global
+ *    state, so calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work and return; results are ready when the stream
+ *    reaches them.  Time them with events on that stream.
+ *  - Arguments are validated on the host before any HIP call.  A negative
+ *    status means nothing was enqueued and no output byte was written.
+ *    QM_ERR_LAUNCH means a HIP launch failed after validation; outputs are
+ *    then unspecified.
+ *  - Outputs are overwritten, never accumulated into.
+ *
+ * Weight formats (the layouts the kernels read directly; no repacking)
+ *  - QM_FMT_INT4: element (r, c) of an n x k matrix is nibble(r, c) - 8 with
+ *    nibble(r, c) = (q[r*k/2 + c/2] >> (4*(c&1))) & 15, i.e. two per byte,
+ *    low nibble first [V: qmatmul.comp note; reading: low nibble = even
+ *    element].  Scales are fp32 [n][k/gs] row-major, one per gs consecutive
+ *    inputs of a row [V: fmt=4 note]; group_size 0 (or k) means one scale per
+ *    row ([n] floats).  gs must be a multiple of 32 that divides k.
+ *  - QM_FMT_INT8_ROW: element (r, c) = (int8_t)q[r*k + c] times scale[r]
+ *    (two's complement, no zero point) [V: qmatmul.comp note, Q: fmt 1].
+ *    group_size must be 0.
+ *  Value = element * its scale.  Accumulation on the GPU is fp32.
+ *
+ * Shape limits of the GPU path (QM_ERR_UNSUPPORTED otherwise): int4 needs
+ * k % 32 == 0, int8 needs k % 16 == 0; 1 <= k <= QM_K_MAX; q and x must be
+ * 16-byte aligned, scales/y 4-byte aligned.  n == 0 is a no-op.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define QM_API __attribute__((visibility("default")))
+#else
+#define QM_API
+#endif
+
+typedef enum {
+  QM_OK = 0,
+  QM_ERR_INVALID = -1,     /* malformed argument: null pointer, negative size, bad enum */
+  QM_ERR_UNSUPPORTED = -2, /* well-formed but outside what the GPU path implements */
+  QM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  QM_ERR_LAUNCH = -4       /* a HIP launch failed */
+} qm_status;
+
+typedef enum { QM_FMT_INT8_ROW = 1, QM_FMT_INT4 = 4 } qm_fmt;
+typedef enum { QM_F32 = 0, QM_BF16 = 1 } qm_dtype;
+
+enum {
+  QM_SMALL_MAX = 8,           /* largest batch of qgemm_small                       */
+  QM_TOPK_MAX = 32,           /* largest top_k of moe_expert_ffn                    */
+  QM_DECODE_MAX_TOKENS = 8,   /* moe_expert_ffn runs the decode kernels up to this  */
+  QM_K_MAX = 1 << 20          /* largest reduction length                           */
+};
+
+/* which kernels moe_expert_ffn_path runs */
+enum { QM_PATH_AUTO = 0, QM_PATH_DECODE = 1, QM_PATH_PREFILL = 2 };
+
+/* A quantized n x k matrix resident on the device. */
+typedef struct {
+  int32_t fmt;        /* qm_fmt                                                */
+  int32_t n, k;       /* outputs (rows), inputs per row                        */
+  int32_t group_size; /* int4: 0 (= per row), k, or a multiple of 32 dividing k */
+  const void *q;      /* device: int4 n*k/2 bytes, int8 n*k bytes, row-major   */
+  const float *scales;/* device: int4 n*(k/gs) (or n) fp32, int8 n fp32       */
+} qm_qmat;
+
+/* E experts stacked expert-major, all in one format and group size.
+ *   gate_q, up_q: [E][inter][hidden] elements (int4: hidden/2 bytes per row)
+ *   down_q:       [E][hidden][inter] elements (int4: inter/2 bytes per row)
+ *   gate_s, up_s: [E][inter][hidden/gs] fp32 (gs 0: [E][inter])
+ *   down_s:       [E][hidden][inter/gs] fp32 (gs 0: [E][hidden])           */
+typedef struct {
+  int32_t n_experts, hidden, inter, fmt, group_size;
+  const void *gate_q, *up_q, *down_q;  /* device */
+  const float *gate_s, *up_s, *down_s; /* device */
+} qm_experts;
+
+/* y[r] = sum_c W[r][c] * x[c], r < w->n.
+ * [V: qmatmul.comp note -- the dense quantized GEMV, one token]
+ * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).       */
+QM_API int qgemv(const qm_qmat *w, const void *x, int32_t x_dtype, float *y, void *stream);
+
+/* Y[t][r] = sum_c W[r][c] * X[t][c] for t < batch, reading W once for all
+ * t.  [V: qmatmul.comp note -- the S-token batch of the same GEMV]
+ * x: device [batch][ldx] (ldx >= k, ldx*elemsize a multiple of 16 bytes).
+ * y: device [batch][ldy] fp32 (ldy >= n).  1 <= batch <= QM_SMALL_MAX.     */
+QM_API int qgemm_small(const qm_qmat *w, const void *x, int32_t x_dtype, int32_t batch, int64_t ldx,
+                float *y, int64_t ldy, void *stream);
+
+/* Bytes of device workspace moe_expert_ffn needs for these sizes (covers
+ * both kernel paths when n_tokens <= QM_DECODE_MAX_TOKENS).  0 on invalid
+ * arguments. */
+QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, int32_t top_k);
+
+/* Routed expert FFN.  For each token t and slot j < top_k, with
+ * e = topk_ids[t][j]:  h = silu(G_e x_t) * (U_e x_t)  and
+ *   y_t = sum_j topk_w[t][j] * (D_e h),  summed in slot order.
+ * [V: qmatmul_gate_up.comp note and the K-expert group note; Q: weighted
+ *  accumulation of the expert outputs; silu(z) = z / (1 + e^-z)]
+ * Gate weights are used as given (no renormalisation).  Each routed
+ * expert's weights are read once per call for all tokens routed to it.
+ * Ids outside [0, n_experts) are skipped (the pair contributes nothing);
+ * the same id twice in one token is summed.
+ * x:         device [n_tokens][hidden] of x_dtype (16-byte aligned rows)
+ * topk_ids:  device int32 [n_tokens][top_k];  topk_w: device fp32 [n_tokens][top_k]
+ * y:         device fp32 [n_tokens][hidden] (overwritten)
+ * workspace: device, >= moe_expert_ffn_workspace(ex, n_tokens, top_k) bytes,
+ *            256-byte aligned; its contents are scratch (not preserved).
+ * n_tokens <= QM_DECODE_MAX_TOKENS runs the decode kernels (fp32 hidden
+ * vector); larger batches run the expert-grouped prefill kernels (bf16 MFMA,
+ * hidden vector and fp32 activations rounded to bf16).                     */
+QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
+                   const int32_t *topk_ids, const float *topk_w, int32_t top_k,
+                   float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_expert_ffn with the kernel path chosen by the caller: QM_PATH_AUTO,
+ * QM_PATH_DECODE (needs n_tokens <= QM_DECODE_MAX_TOKENS) or
+ * QM_PATH_PREFILL (any n_tokens).                                          */
+QM_API int moe_expert_ffn_path(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
+                        const int32_t *topk_ids, const float *topk_w, int32_t top_k,
+                        float *y, void *workspace, size_t workspace_bytes, void *stream,
+                        int32_t path);
+
+/* Stage 1 of the decode path on its own (the fused gate+up dispatch of the
+ * "qmatmul_gate_up.comp" commit note [V]): for every pair p = t*top_k + j
+ * with a valid id e, h[p][:] = silu(G_e x_t) * (U_e x_t).  Rows of pairs with
+ * an invalid id are not written.  Needs n_tokens <= QM_DECODE_MAX_TOKENS.
+ * h: device fp32 [n_tokens*top_k][inter], 4-byte aligned.                   */
+QM_API int moe_gate_up(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
+                       const int32_t *topk_ids, int32_t top_k, float *h, void *stream);
+
+/* Stage 2 of the decode path on its own: y_t = sum_j topk_w[t][j] *
+ * (D_e h[t*top_k + j]) in slot order, from the hidden rows that moe_gate_up
+ * wrote.  h: device fp32 [n_tokens*top_k][inter], 16-byte aligned;
+ * workspace as for moe_expert_ffn.  moe_gate_up followed by moe_down on one
+ * stream computes exactly what moe_expert_ffn computes for these sizes.    */
+QM_API int moe_down(const qm_experts *ex, const float *h, int32_t n_tokens, const int32_t *topk_ids,
+                    const float *topk_w, int32_t top_k, float *y, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Static text for a qm_status value. */
+QM_API const char *qm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,59 @@
+"""Build libqmoe.so (hand-written HIP for gfx950) in-tree with hipcc.
+
+Every csrc/*.hip file is compiled for gfx950 only (packed-fp32 instructions
+disabled) into an object under _build/, in parallel, and the objects are
+linked into one shared object that exports the C ABI of include/qmoe.h.
+Run `python -m int4_expert_gemv_amd.build`.
+"""
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libqmoe.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def _compile(src, extra):
+    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", "-o", obj, src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops' is not a recognized" not in l]
+    if r.returncode:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, "\n".join(msgs)))
+    return obj, msgs
+
+
+def build(out=LIB, verbose=False, extra=(), jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+    for obj, msgs in results:
+        if verbose and msgs:
+            print("\n".join(msgs))
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                    *[o for o, _ in results]], check=True)
+    os.replace(tmp, out)
+    if verbose:
+        print("built", out, flush=True)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

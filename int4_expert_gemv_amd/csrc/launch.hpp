@@ -1,0 +1,91 @@
+// launch.hpp -- kernel argument blocks and host-side launchers shared by the
+// C ABI (qmoe.hip) and the kernel files.  Internal to libqmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qm {
+
+struct GemvArgs {
+  const uint8_t* q;   // packed weights, row-major
+  const float* s;     // scales: [n][G] (grouped) or [n]
+  const void* x;      // activations [nb][ldx]
+  float* y;           // outputs [nb][ldy]
+  int n, k;
+  int G, gshift;      // groups per row; chunk index >> gshift = group (grouped int4)
+  int64_t row_bytes, ldx, ldy;
+  int nb;             // batch actually used
+  int segc;           // chunks per LDS segment (set by the launcher)
+  int rounds;         // tiles per wave
+};
+
+// One set of stacked experts as seen by the kernels.
+struct ExpertArgs {
+  const uint8_t *gq, *uq, *dq;
+  const float *gs, *us, *ds;
+  int E, H, I;
+  int G_h, G_i;       // scale groups per gate/up row (K = H) and per down row (K = I)
+  int gshift;         // log2(group size / 32) for grouped int4
+  int64_t rb_h, rb_i; // bytes per gate/up row and per down row
+};
+
+struct MoeDecodeArgs {
+  ExpertArgs ex;
+  const void* x;       // [T][H]
+  const int32_t* ids;  // [T][k]
+  const float* w;      // [T][k]
+  float* h;            // workspace [T*k][I] fp32
+  float* pout;         // workspace [T*k][H] fp32, per-pair down outputs
+  float* y;            // [T][H]
+  int T, topk;
+  int segc;            // chunks per LDS segment
+  int parts;           // blocks per unique expert
+  int rounds;          // tiles per wave
+};
+
+// qgemv.hip
+int lanes_per_row(int kchunks);
+int rows_per_unit(int L, int NB);
+int seg_chunks(int fmt, int xdt, int NB, int kchunks);
+size_t stage_bytes(int fmt, int xdt, int NB, int segc);
+hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a, int NB, hipStream_t st);
+hipError_t launch_fill_zero(float* y, int64_t n, int64_t ld, int rows, hipStream_t st);
+
+// per-instantiation launchers (qgemv_*.hip): grouped (_g) or row-scaled (_r)
+#define QM_DECL_QGEMV(name) \
+  hipError_t name(const GemvArgs& a, int L, int NB, int blocks, size_t lds, hipStream_t st);
+QM_DECL_QGEMV(qgemv_launch_i4_bf16_g)
+QM_DECL_QGEMV(qgemv_launch_i4_bf16_r)
+QM_DECL_QGEMV(qgemv_launch_i4_f32_g)
+QM_DECL_QGEMV(qgemv_launch_i4_f32_r)
+QM_DECL_QGEMV(qgemv_launch_i8_bf16_r)
+QM_DECL_QGEMV(qgemv_launch_i8_f32_r)
+#undef QM_DECL_QGEMV
+
+// moe_decode_*.hip: stage launchers per (format, activation type, grouping)
+#define QM_DECL_MOE(name) hipError_t name(const MoeDecodeArgs& a, hipStream_t st);
+QM_DECL_MOE(moe_gate_up_i4_bf16_g)
+QM_DECL_MOE(moe_gate_up_i4_bf16_r)
+QM_DECL_MOE(moe_gate_up_i4_f32_g)
+QM_DECL_MOE(moe_gate_up_i4_f32_r)
+QM_DECL_MOE(moe_gate_up_i8_bf16_r)
+QM_DECL_MOE(moe_gate_up_i8_f32_r)
+QM_DECL_MOE(moe_down_i4_g)
+QM_DECL_MOE(moe_down_i4_r)
+QM_DECL_MOE(moe_down_i8_r)
+#undef QM_DECL_MOE
+
+// moe_decode.hip
+hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
+hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
+
+// moe_prefill.hip
+struct MoePrefillArgs;
+size_t moe_prefill_workspace(int T, int topk, int E, int H, int I);
+hipError_t launch_moe_prefill(int fmt, int xdt, bool grouped, const ExpertArgs& ex, const void* x,
+                              const int32_t* ids, const float* w, int T, int topk, float* y, void* ws,
+                              hipStream_t st);
+
+}  // namespace qm

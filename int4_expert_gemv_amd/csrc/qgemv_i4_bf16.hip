@@ -1,0 +1,15 @@
+// qgemv_i4_bf16.hip -- instantiations of the quantized GEMV kernel for one
+// (format, activation type) pair.
+#include "qgemv_impl.hpp"
+
+namespace qm {
+
+hipError_t qgemv_launch_i4_bf16_g(const GemvArgs& a, int L, int NB, int blocks, size_t lds, hipStream_t st) {
+  return launch_g<kFmtInt4, kBF16, true>(a, L, NB, blocks, lds, st);
+}
+
+hipError_t qgemv_launch_i4_bf16_r(const GemvArgs& a, int L, int NB, int blocks, size_t lds, hipStream_t st) {
+  return launch_g<kFmtInt4, kBF16, false>(a, L, NB, blocks, lds, st);
+}
+
+}  // namespace qm

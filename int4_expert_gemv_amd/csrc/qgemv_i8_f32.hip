@@ -1,0 +1,11 @@
+// qgemv_i8_f32.hip -- instantiations of the quantized GEMV kernel for one
+// (format, activation type) pair.
+#include "qgemv_impl.hpp"
+
+namespace qm {
+
+hipError_t qgemv_launch_i8_f32_r(const GemvArgs& a, int L, int NB, int blocks, size_t lds, hipStream_t st) {
+  return launch_g<kFmtInt8, kF32, false>(a, L, NB, blocks, lds, st);
+}
+
+}  // namespace qm

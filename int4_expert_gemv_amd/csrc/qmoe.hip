@@ -1,0 +1,288 @@
+// qmoe.hip -- the C ABI of libqmoe.so (declared in include/qmoe.h).
+//
+// Every entry point validates its arguments on the host before the first HIP
+// call; a rejected call enqueues nothing and writes nothing (the colibri page
+// "qwen36: Vulkan expert tier, and staged device-local uploads" keeps the
+// caller's output untouched when the GPU path refuses a request).
+#include "../../include/qmoe.h"
+#include "launch.hpp"
+
+#include <limits.h>
+
+namespace {
+
+using namespace qm;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return (1 << r) == v ? r : -1;
+}
+
+// Effective group size: 0 means one scale per row.
+int eff_gs(int fmt, int gs, int k) { return (fmt == QM_FMT_INT4 && gs > 0 && gs < k) ? gs : 0; }
+
+// Shape checks for one n x k matrix in (fmt, gs).  Returns a qm_status.
+int check_shape(int fmt, int n, int k, int gs) {
+  if (fmt != QM_FMT_INT4 && fmt != QM_FMT_INT8_ROW) return QM_ERR_INVALID;
+  if (n < 0 || k < 0 || gs < 0) return QM_ERR_INVALID;
+  if (fmt == QM_FMT_INT4 && (k & 1)) return QM_ERR_INVALID;
+  if (fmt == QM_FMT_INT8_ROW && gs != 0) return QM_ERR_INVALID;
+  if (k == 0 || k > QM_K_MAX) return QM_ERR_UNSUPPORTED;
+  if (fmt == QM_FMT_INT4 && k % 32) return QM_ERR_UNSUPPORTED;
+  if (fmt == QM_FMT_INT8_ROW && k % 16) return QM_ERR_UNSUPPORTED;
+  const int g = eff_gs(fmt, gs, k);
+  if (g) {
+    if (g % 32 || k % g || ilog2(g / 32) < 0) return QM_ERR_UNSUPPORTED;
+  } else if (fmt == QM_FMT_INT4 && gs > k) {
+    return QM_ERR_UNSUPPORTED;
+  }
+  return QM_OK;
+}
+
+int64_t row_bytes(int fmt, int k) { return fmt == QM_FMT_INT4 ? (int64_t)k / 2 : (int64_t)k; }
+
+int groups(int fmt, int gs, int k) {
+  const int g = eff_gs(fmt, gs, k);
+  return g ? k / g : 1;
+}
+
+int xsize(int dt) { return dt == QM_BF16 ? 2 : 4; }
+
+int check_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_t ldx, const float* y,
+               int64_t ldy) {
+  if (!w) return QM_ERR_INVALID;
+  if (xdt != QM_F32 && xdt != QM_BF16) return QM_ERR_INVALID;
+  if (batch < 1) return QM_ERR_INVALID;
+  int st = check_shape(w->fmt, w->n, w->k, w->group_size);
+  if (st == QM_ERR_INVALID) return st;
+  if (w->n == 0) return QM_OK;  // nothing to compute (pointers may be null)
+  if (!w->q || !w->scales || !x || !y) return QM_ERR_INVALID;
+  if (ldx < w->k || ldy < w->n) return QM_ERR_INVALID;
+  if (st != QM_OK) return st;
+  if (batch > QM_SMALL_MAX) return QM_ERR_UNSUPPORTED;
+  if (!aligned(w->q, 16) || !aligned(x, 16) || !aligned(w->scales, 4) || !aligned(y, 4))
+    return QM_ERR_UNSUPPORTED;
+  if ((ldx * xsize(xdt)) % 16) return QM_ERR_UNSUPPORTED;
+  return QM_OK;
+}
+
+int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_t ldx, float* y, int64_t ldy,
+             void* stream) {
+  int st = check_gemm(w, x, xdt, batch, ldx, y, ldy);
+  if (st != QM_OK || w->n == 0) return st;
+  const int g = eff_gs(w->fmt, w->group_size, w->k);
+  GemvArgs a{};
+  a.q = static_cast<const uint8_t*>(w->q);
+  a.s = w->scales;
+  a.x = x;
+  a.y = y;
+  a.n = w->n;
+  a.k = w->k;
+  a.G = groups(w->fmt, w->group_size, w->k);
+  a.gshift = g ? ilog2(g / 32) : 0;
+  a.row_bytes = row_bytes(w->fmt, w->k);
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.nb = batch;
+  a.rounds = 1;
+  const int NB = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
+  hipError_t err = launch_qgemv(w->fmt, xdt, g != 0, a, NB, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+}
+
+// ---- MoE -------------------------------------------------------------------------
+
+int check_experts(const qm_experts* ex) {
+  if (!ex) return QM_ERR_INVALID;
+  if (ex->n_experts < 1 || ex->hidden < 0 || ex->inter < 0) return QM_ERR_INVALID;
+  int a = check_shape(ex->fmt, ex->inter, ex->hidden, ex->group_size);
+  int b = check_shape(ex->fmt, ex->hidden, ex->inter, ex->group_size);
+  if (a == QM_ERR_INVALID || b == QM_ERR_INVALID) return QM_ERR_INVALID;
+  if (!ex->gate_q || !ex->up_q || !ex->down_q || !ex->gate_s || !ex->up_s || !ex->down_s) return QM_ERR_INVALID;
+  if (a != QM_OK) return a;
+  if (b != QM_OK) return b;
+  if (ex->hidden < 1 || ex->inter < 1) return QM_ERR_UNSUPPORTED;
+  const void* q[3] = {ex->gate_q, ex->up_q, ex->down_q};
+  const void* s[3] = {ex->gate_s, ex->up_s, ex->down_s};
+  for (int i = 0; i < 3; ++i)
+    if (!aligned(q[i], 16) || !aligned(s[i], 4)) return QM_ERR_UNSUPPORTED;
+  return QM_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t decode_workspace(int T, int k, int H, int I) {
+  const size_t P = (size_t)T * k;
+  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256);
+}
+
+ExpertArgs expert_args(const qm_experts* ex) {
+  ExpertArgs e{};
+  e.gq = static_cast<const uint8_t*>(ex->gate_q);
+  e.uq = static_cast<const uint8_t*>(ex->up_q);
+  e.dq = static_cast<const uint8_t*>(ex->down_q);
+  e.gs = ex->gate_s;
+  e.us = ex->up_s;
+  e.ds = ex->down_s;
+  e.E = ex->n_experts;
+  e.H = ex->hidden;
+  e.I = ex->inter;
+  e.G_h = groups(ex->fmt, ex->group_size, ex->hidden);
+  e.G_i = groups(ex->fmt, ex->group_size, ex->inter);
+  const int g = eff_gs(ex->fmt, ex->group_size, ex->hidden);
+  e.gshift = g ? ilog2(g / 32) : 0;
+  e.rb_h = row_bytes(ex->fmt, ex->hidden);
+  e.rb_i = row_bytes(ex->fmt, ex->inter);
+  return e;
+}
+
+// Decode workspace: h [T*k][I] fp32, then per-pair down outputs [T*k][H] fp32.
+MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32_t* ids, const float* w, int k,
+                          float* y, void* workspace) {
+  MoeDecodeArgs a{};
+  a.ex = e;
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  char* ws = static_cast<char*>(workspace);
+  a.h = reinterpret_cast<float*>(ws);
+  a.pout = reinterpret_cast<float*>(ws + align_up((size_t)T * k * e.I * 4, 256));
+  a.y = y;
+  a.T = T;
+  a.topk = k;
+  a.rounds = 1;
+  return a;
+}
+
+// grouped iff both projections' reduction lengths are split into groups
+int moe_grouping(const qm_experts* ex, bool* grouped) {
+  const int gh = eff_gs(ex->fmt, ex->group_size, ex->hidden);
+  const int gi = eff_gs(ex->fmt, ex->group_size, ex->inter);
+  if ((gh == 0) != (gi == 0)) return QM_ERR_UNSUPPORTED;  // grouped along one reduction only
+  *grouped = gh != 0;
+  return QM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qm_strerror(int status) {
+  switch (status) {
+    case QM_OK: return "ok";
+    case QM_ERR_INVALID: return "invalid argument";
+    case QM_ERR_UNSUPPORTED: return "unsupported shape, format or alignment for the GPU path";
+    case QM_ERR_WORKSPACE: return "workspace missing or too small";
+    case QM_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int qgemv(const qm_qmat* w, const void* x, int32_t x_dtype, float* y, void* stream) {
+  return run_gemm(w, x, x_dtype, 1, w ? w->k : 0, y, w ? w->n : 0, stream);
+}
+
+int qgemm_small(const qm_qmat* w, const void* x, int32_t x_dtype, int32_t batch, int64_t ldx, float* y,
+                int64_t ldy, void* stream) {
+  return run_gemm(w, x, x_dtype, batch, ldx, y, ldy, stream);
+}
+
+size_t moe_expert_ffn_workspace(const qm_experts* ex, int32_t n_tokens, int32_t top_k) {
+  if (!ex || n_tokens < 0 || top_k < 1 || top_k > QM_TOPK_MAX) return 0;
+  if (ex->hidden < 1 || ex->inter < 1 || ex->n_experts < 1) return 0;
+  size_t need = moe_prefill_workspace(n_tokens, top_k, ex->n_experts, ex->hidden, ex->inter);
+  if (n_tokens <= QM_DECODE_MAX_TOKENS) {
+    const size_t d = decode_workspace(n_tokens, top_k, ex->hidden, ex->inter);
+    if (d > need) need = d;
+  }
+  return need < 256 ? 256 : need;
+}
+
+int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens,
+                        const int32_t* topk_ids, const float* topk_w, int32_t top_k, float* y, void* workspace,
+                        size_t workspace_bytes, void* stream, int32_t path) {
+  if (path != QM_PATH_AUTO && path != QM_PATH_DECODE && path != QM_PATH_PREFILL) return QM_ERR_INVALID;
+  if (x_dtype != QM_F32 && x_dtype != QM_BF16) return QM_ERR_INVALID;
+  if (n_tokens < 0 || top_k < 1) return QM_ERR_INVALID;
+  int st = check_experts(ex);
+  if (st == QM_ERR_INVALID) return st;
+  if (n_tokens == 0) return QM_OK;
+  if (!x || !topk_ids || !topk_w || !y) return QM_ERR_INVALID;
+  if (st != QM_OK) return st;
+  if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
+  if (path == QM_PATH_AUTO) path = n_tokens <= QM_DECODE_MAX_TOKENS ? QM_PATH_DECODE : QM_PATH_PREFILL;
+  if (path == QM_PATH_DECODE && n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
+  bool grouped = false;
+  st = moe_grouping(ex, &grouped);
+  if (st != QM_OK) return st;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+    return QM_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ExpertArgs e = expert_args(ex);
+  hipError_t err;
+  if (path == QM_PATH_DECODE) {
+    MoeDecodeArgs a = decode_args(e, x, n_tokens, topk_ids, topk_w, top_k, y, workspace);
+    err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
+    if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
+  } else {
+    err = launch_moe_prefill(ex->fmt, x_dtype, grouped, e, x, topk_ids, topk_w, n_tokens, top_k, y, workspace, s);
+  }
+  if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
+  return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+}
+
+int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_ids,
+                int32_t top_k, float* h, void* stream) {
+  if (x_dtype != QM_F32 && x_dtype != QM_BF16) return QM_ERR_INVALID;
+  if (n_tokens < 0 || top_k < 1) return QM_ERR_INVALID;
+  int st = check_experts(ex);
+  if (st == QM_ERR_INVALID) return st;
+  if (n_tokens == 0) return QM_OK;
+  if (!x || !topk_ids || !h) return QM_ERR_INVALID;
+  if (st != QM_OK) return st;
+  if (top_k > QM_TOPK_MAX || n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(h, 4) || !aligned(topk_ids, 4)) return QM_ERR_UNSUPPORTED;
+  bool grouped = false;
+  st = moe_grouping(ex, &grouped);
+  if (st != QM_OK) return st;
+  MoeDecodeArgs a = decode_args(expert_args(ex), x, n_tokens, topk_ids, nullptr, top_k, nullptr, nullptr);
+  a.h = h;
+  hipError_t err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+}
+
+int moe_down(const qm_experts* ex, const float* h, int32_t n_tokens, const int32_t* topk_ids, const float* topk_w,
+             int32_t top_k, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0 || top_k < 1) return QM_ERR_INVALID;
+  int st = check_experts(ex);
+  if (st == QM_ERR_INVALID) return st;
+  if (n_tokens == 0) return QM_OK;
+  if (!h || !topk_ids || !topk_w || !y) return QM_ERR_INVALID;
+  if (st != QM_OK) return st;
+  if (top_k > QM_TOPK_MAX || n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
+  if (!aligned(h, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
+  bool grouped = false;
+  st = moe_grouping(ex, &grouped);
+  if (st != QM_OK) return st;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+    return QM_ERR_WORKSPACE;
+  MoeDecodeArgs a = decode_args(expert_args(ex), nullptr, n_tokens, topk_ids, topk_w, top_k, y, workspace);
+  a.h = const_cast<float*>(h);
+  hipError_t err = launch_moe_down(ex->fmt, grouped, a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+}
+
+int moe_expert_ffn(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens,
+                   const int32_t* topk_ids, const float* topk_w, int32_t top_k, float* y, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return moe_expert_ffn_path(ex, x, x_dtype, n_tokens, topk_ids, topk_w, top_k, y, workspace, workspace_bytes,
+                             stream, QM_PATH_AUTO);
+}
+
+}  // extern "C"

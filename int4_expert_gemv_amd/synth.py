@@ -8,8 +8,10 @@ bf16 activations are fp32 draws rounded by torch's own conversion.
 
 Every tensor of an expert set comes from its own PCG64 stream keyed by
 (seed, tensor, expert), so any single expert can be regenerated without
-drawing the others.
+drawing the others, and a large stack can be drawn on several threads.
 """
+import concurrent.futures
+
 import numpy as np
 import torch
 
@@ -33,14 +35,19 @@ def quant_matrix(g, fmt, n, k, gs, scale_lo=0.005, scale_hi=0.02):
     """(q, scales) for an n x k matrix: int4 -> uint8 [n][k/2] uniform bytes;
     int8 -> int8 [n][k] uniform in [-127, 127].  Scales U(lo, hi) fp32."""
     if fmt == FMT_INT4:
-        q = np.frombuffer(g.bytes(n * (k // 2)), dtype=np.uint8).reshape(n, k // 2).copy()
-        s = g.uniform(scale_lo, scale_hi, size=(n, n_groups(k, gs))).astype(np.float32)
+        q = g.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        s = uniform_f32(g, (n, n_groups(k, gs)), scale_lo, scale_hi)
     elif fmt == FMT_INT8_ROW:
-        q = g.integers(-127, 128, size=(n, k), dtype=np.int16).astype(np.int8)
-        s = g.uniform(scale_lo, scale_hi, size=(n, 1)).astype(np.float32)
+        q = g.integers(-127, 128, size=(n, k), dtype=np.int8)
+        s = uniform_f32(g, (n, 1), scale_lo, scale_hi)
     else:
         raise ValueError(fmt)
     return q, s
+
+
+def uniform_f32(g, shape, lo, hi):
+    """fp32 draws in [lo, hi)."""
+    return g.random(size=shape, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
 
 
 def normal_f32(g, shape):
@@ -99,7 +106,7 @@ def zipf_routing(g, n_tokens, n_experts, top_k, alpha=1.1):
     return ids.astype(np.int32), w.astype(np.float32)
 
 
-def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None):
+def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None, threads=1):
     """Stacked expert weights as a dict (the layout the library and the oracle
     both take).  `experts` limits generation to a subset of ids; the other
     experts' slots are left zero (only valid when routing avoids them)."""
@@ -118,10 +125,19 @@ def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None):
         "up_s": np.zeros((n_experts, inter, G_h), np.float32),
         "down_s": np.zeros((n_experts, hidden, G_i), np.float32),
     }
-    for e in (range(n_experts) if experts is None else sorted(set(int(i) for i in experts))):
+    ids = range(n_experts) if experts is None else sorted(set(int(i) for i in experts if 0 <= i < n_experts))
+
+    def fill(e):
         for tag, name, n, k in ((_T_GATE, "gate", inter, hidden), (_T_UP, "up", inter, hidden),
                                 (_T_DOWN, "down", hidden, inter)):
             q, s = quant_matrix(rng(seed, tag, e), fmt, n, k, gs)
             out[name + "_q"][e] = q
             out[name + "_s"][e] = s.reshape(out[name + "_s"][e].shape)
+
+    if threads > 1 and len(ids) > 1:
+        with concurrent.futures.ThreadPoolExecutor(threads) as pool:
+            list(pool.map(fill, ids))
+    else:
+        for e in ids:
+            fill(e)
     return out

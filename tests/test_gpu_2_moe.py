@@ -1,0 +1,112 @@
+"""GPU parity of moe_expert_ffn against the fp64 oracle.
+
+Bar: max over outputs of |y_gpu - y_oracle| / N(t, i) <= 2e-4 where
+N(t, i) = sum_j |w_tj| * sum_m |d_{e,i,m} h_{tj,m}| (the normaliser of the
+final contraction, from the oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, dev, host, norm_err, upload_experts
+from int4_expert_gemv_amd import synth
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    from int4_expert_gemv_amd import qmoe
+    assert torch.cuda.is_available()
+    return qmoe
+
+
+def _routing(seed, T, E, k, kind="uniform"):
+    g = np.random.default_rng([seed, 7])
+    if kind == "zipf":
+        return synth.zipf_routing(g, T, E, k)
+    return synth.uniform_routing(g, T, E, k)
+
+
+def run_moe(q, ex, d, x, ids, w, path=0):
+    T, k = ids.shape
+    e = q.experts(ex["fmt"], ex["gs"], d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
+    ws = torch.empty(max(q.moe_expert_ffn_workspace(e, T, k), 256), dtype=torch.uint8, device="cuda")
+    y = torch.full((T, ex["hidden"]), float("nan"), device="cuda")
+    q.moe_expert_ffn(e, dev(x), dev(ids), dev(w), y, ws, path=path)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def _check(q, oracle, seed, fmt, gs, E, H, I, T, k, xdt="bf16", kind="uniform", path=0, flags=0):
+    print("moe parity fmt=%d gs=%d E=%d H=%d I=%d T=%d k=%d x=%s %s path=%d" %
+          (fmt, gs, E, H, I, T, k, xdt, kind, path), flush=True)
+    ids, w = _routing(seed, T, E, k, kind)
+    ex = synth.expert_set(seed, fmt, E, H, I, gs, experts=np.unique(ids))
+    d = upload_experts(ex, only=np.unique(ids))
+    x = synth.activations(np.random.default_rng([seed, 8]), (T, H), xdt)
+    y = run_moe(q, ex, d, x, ids, w, path)
+    yr, _, nr = oracle.moe_ffn(ex, x, ids, w, flags=flags)
+    err = norm_err(y, yr, nr)
+    assert err <= TOL, err
+    return y
+
+
+def test_moe_35b_like_decode(q, oracle):
+    """hidden 2048, 256 experts, intermediate 512, top-8, one token, int4-g64."""
+    _check(q, oracle, 0, 4, 64, 256, 2048, 512, 1, 8)
+
+
+@pytest.mark.parametrize("gs", [64, 0])
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_moe_large_decode(q, oracle, gs, T):
+    """hidden 6144, 320 experts, intermediate 2048, top-8, 1..8 tokens."""
+    _check(q, oracle, 1, 4, gs, 320, 6144, 2048, T, 8)
+
+
+def test_moe_int8_experts(q, oracle):
+    _check(q, oracle, 2, 1, 0, 16, 1024, 512, 3, 4)
+
+
+def test_moe_fp32_activations(q, oracle):
+    _check(q, oracle, 3, 4, 64, 32, 2048, 512, 2, 8, xdt="f32")
+
+
+def test_moe_shared_experts_across_tokens(q, oracle):
+    """Zipf routing over few experts: most experts serve several tokens."""
+    _check(q, oracle, 4, 4, 64, 16, 2048, 1024, 8, 6, kind="zipf")
+
+
+def test_moe_small_and_ragged(q, oracle):
+    _check(q, oracle, 5, 4, 0, 5, 96, 160, 3, 2)
+    _check(q, oracle, 6, 4, 32, 7, 256, 96, 5, 3)
+
+
+def test_moe_topk_32(q, oracle):
+    _check(q, oracle, 7, 4, 64, 64, 512, 256, 8, 32)
+
+
+def test_moe_invalid_and_duplicate_ids(q, oracle):
+    E, H, I, T, k = 12, 512, 256, 3, 4
+    ids, w = _routing(8, T, E, k)
+    ids[0, 1] = E + 3       # out of range: skipped
+    ids[1, 2] = -1          # negative: skipped
+    ids[2, 3] = ids[2, 0]   # same expert twice in one token: summed
+    ex = synth.expert_set(8, 4, E, H, I, 64)
+    d = upload_experts(ex)
+    x = synth.activations(np.random.default_rng(9), (T, H), "bf16")
+    y = run_moe(q, ex, d, x, ids, w)
+    yr, _, nr = oracle.moe_ffn(ex, x, ids, w)
+    assert norm_err(y, yr, nr) <= TOL
+
+
+def test_moe_deterministic(q):
+    E, H, I, T, k = 64, 2048, 1024, 4, 8
+    ids, w = _routing(10, T, E, k)
+    ex = synth.expert_set(10, 4, E, H, I, 64, experts=np.unique(ids))
+    d = upload_experts(ex, only=np.unique(ids))
+    x = synth.activations(np.random.default_rng(11), (T, H), "bf16")
+    y1 = run_moe(q, ex, d, x, ids, w)
+    y2 = run_moe(q, ex, d, x, ids, w)
+    assert np.array_equal(y1, y2)
