@@ -35,7 +35,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "gemv"])
+    p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "gemv", "copy"],
+                   help="copy: a plain 1 GiB device-to-device copy, the reference kernel for scaling the "
+                        "FETCH_SIZE / WRITE_SIZE counters")
     p.add_argument("--tokens", type=int, default=1)
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
     p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
@@ -212,6 +214,29 @@ def bench_gemv(args):
             "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None}
 
 
+def bench_copy(args):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    return {"metric": "device copy bandwidth (read + write)", "value": round(2 * n / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "1 GiB device-to-device copy"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -224,6 +249,8 @@ def main():
         out = bench_moe(args, 320, 6144, 2048)
     elif args.config == "moe_35b":
         out = bench_moe(args, 256, 2048, 512)
+    elif args.config == "copy":
+        out = bench_copy(args)
     else:
         out = bench_gemv(args)
     print(json.dumps(out), flush=True)
