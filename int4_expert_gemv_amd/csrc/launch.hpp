@@ -19,6 +19,7 @@ struct GemvArgs {
   int nb;             // batch actually used
   int segc;           // chunks per LDS segment (set by the launcher)
   int rounds;         // tiles per wave
+  int max_blocks;     // pipelined kernels: grid size cap (0 = default)
 };
 
 // One set of stacked experts as seen by the kernels.
@@ -43,6 +44,7 @@ struct MoeDecodeArgs {
   int segc;            // chunks per LDS segment
   int parts;           // blocks per unique expert
   int rounds;          // tiles per wave
+  int max_blocks;      // pipelined kernels: grid size cap (0 = default)
 };
 
 // qgemv.hip
@@ -62,7 +64,17 @@ QM_DECL_QGEMV(qgemv_launch_i4_f32_g)
 QM_DECL_QGEMV(qgemv_launch_i4_f32_r)
 QM_DECL_QGEMV(qgemv_launch_i8_bf16_r)
 QM_DECL_QGEMV(qgemv_launch_i8_f32_r)
+#define QM_DECL_QGEMV2(name) \
+  hipError_t name(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st);
+QM_DECL_QGEMV2(qgemv_v2_i4_bf16_g)
+QM_DECL_QGEMV2(qgemv_v2_i4_bf16_r)
+QM_DECL_QGEMV2(qgemv_v2_i8_bf16_r)
+#undef QM_DECL_QGEMV2
 #undef QM_DECL_QGEMV
+
+// v2 (pipelined, single token, whole x in LDS) shape choices
+int v2_cb(int kchunks, int L);
+int v2_blocks(int ntiles, int max_blocks);
 
 // moe_decode_*.hip: stage launchers per (format, activation type, grouping)
 #define QM_DECL_MOE(name) hipError_t name(const MoeDecodeArgs& a, hipStream_t st);

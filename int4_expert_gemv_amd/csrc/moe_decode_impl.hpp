@@ -243,6 +243,182 @@ inline hipError_t launch_down(const MoeDecodeArgs& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+// ---- pipelined single-token kernels --------------------------------------------
+// One batch slot (NB = 1): every pair of a distinct expert is processed in
+// turn with the whole activation row staged in LDS; each wave walks its tiles
+// with the next unit's weights in flight (see pipeline_tiles).
+
+constexpr int ru_for(int M, int CB) {
+  return 8 / (M * CB) >= 8 ? 8 : (8 / (M * CB) >= 4 ? 4 : (8 / (M * CB) >= 2 ? 2 : 1));
+}
+
+template <int FMT, int XT, int L, int CB, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void moe_gate_up_v2_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_ids[kMaxPairs], s_flag[kMaxPairs], s_pairs[kMaxPairs], s_misc[2];
+  constexpr bool SPLIT = (FMT == kFmtInt4 && XT == kF32);
+  constexpr int RU = ru_for(2, CB);
+  constexpr int RPW = 64 / L;
+  constexpr int TILE = RPW * RU;
+  const ExpertArgs& ex = a.ex;
+  const int u = blockIdx.x / a.parts, part = blockIdx.x - u * a.parts;
+  const int e = route_unique(a.ids, a.T * a.topk, ex.E, u, s_ids, s_flag, s_pairs, s_misc);
+  if (e < 0) return;
+  const int npairs = s_misc[1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane / L;
+  const int kchunks = ex.H / Fmt<FMT>::kPerChunk;
+  const int ntiles = (ex.I + TILE - 1) / TILE;
+  const int npasses = (kchunks + L * CB - 1) / (L * CB);
+  const int tile0 = part * kWaves + wave, tstride = a.parts * kWaves;
+  Mats<2> mt;
+  mt.q[0] = ex.gq + (int64_t)e * ex.I * ex.rb_h;
+  mt.q[1] = ex.uq + (int64_t)e * ex.I * ex.rb_h;
+  mt.s[0] = ex.gs + (int64_t)e * ex.I * ex.G_h;
+  mt.s[1] = ex.us + (int64_t)e * ex.I * ex.G_h;
+  for (int pb = 0; pb < npairs; ++pb) {
+    const int pair = s_pairs[pb];
+    const int tok = pair / a.topk;
+    TileW<2, RU, CB> A, B;
+    if (tile0 < ntiles)
+      unit_load<FMT, L, 2, RU, CB, GROUPED>(A, mt, ex.rb_h, ex.G_h, ex.gshift, tile0 * TILE + lrow, RPW, ex.I,
+                                            kchunks, 0);
+    if (pb > 0) __syncthreads();
+    stage_x<FMT, XT, 1>(lds, a.x, ex.H, [tok](int) { return tok; }, 0, kchunks);
+    __syncthreads();
+    pipeline_tiles<FMT, SPLIT, L, 2, RU, CB, 1, GROUPED>(
+        A, B, mt, ex.rb_h, ex.G_h, ex.gshift, ex.I, kchunks, tile0, tstride, ntiles, npasses, lds,
+        [&](int tile, float (&acc)[2][RU][1]) {
+#pragma unroll
+          for (int j = 0; j < RU; ++j) {
+            const int r = tile * TILE + lrow + j * RPW;
+            const bool ok = r < ex.I;
+            const float gsr = (!GROUPED && ok) ? mt.s[0][r] : 1.0f;
+            const float usr = (!GROUPED && ok) ? mt.s[1][r] : 1.0f;
+            const float g = group_sum<L>(acc[0][j][0]) * gsr;
+            const float v = group_sum<L>(acc[1][j][0]) * usr;
+            if ((lane % L) == 0 && ok) a.h[(int64_t)pair * ex.I + r] = silu(g) * v;
+          }
+        });
+  }
+}
+
+template <int FMT, int L, int CB, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void moe_down_v2_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_ids[kMaxPairs], s_flag[kMaxPairs], s_pairs[kMaxPairs], s_misc[2];
+  constexpr bool SPLIT = (FMT == kFmtInt4);
+  constexpr int RU = ru_for(1, CB);
+  constexpr int RPW = 64 / L;
+  constexpr int TILE = RPW * RU;
+  const ExpertArgs& ex = a.ex;
+  const int u = blockIdx.x / a.parts, part = blockIdx.x - u * a.parts;
+  const int e = route_unique(a.ids, a.T * a.topk, ex.E, u, s_ids, s_flag, s_pairs, s_misc);
+  if (e < 0) return;
+  const int npairs = s_misc[1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane / L;
+  const int kchunks = ex.I / Fmt<FMT>::kPerChunk;
+  const int ntiles = (ex.H + TILE - 1) / TILE;
+  const int npasses = (kchunks + L * CB - 1) / (L * CB);
+  const int tile0 = part * kWaves + wave, tstride = a.parts * kWaves;
+  Mats<1> mt;
+  mt.q[0] = ex.dq + (int64_t)e * ex.H * ex.rb_i;
+  mt.s[0] = ex.ds + (int64_t)e * ex.H * ex.G_i;
+  for (int pb = 0; pb < npairs; ++pb) {
+    const int pair = s_pairs[pb];
+    TileW<1, RU, CB> A, B;
+    if (tile0 < ntiles)
+      unit_load<FMT, L, 1, RU, CB, GROUPED>(A, mt, ex.rb_i, ex.G_i, ex.gshift, tile0 * TILE + lrow, RPW, ex.H,
+                                            kchunks, 0);
+    if (pb > 0) __syncthreads();
+    stage_x<FMT, kF32, 1>(lds, a.h, ex.I, [pair](int) { return pair; }, 0, kchunks);
+    __syncthreads();
+    pipeline_tiles<FMT, SPLIT, L, 1, RU, CB, 1, GROUPED>(
+        A, B, mt, ex.rb_i, ex.G_i, ex.gshift, ex.H, kchunks, tile0, tstride, ntiles, npasses, lds,
+        [&](int tile, float (&acc)[1][RU][1]) {
+#pragma unroll
+          for (int j = 0; j < RU; ++j) {
+            const int r = tile * TILE + lrow + j * RPW;
+            const bool ok = r < ex.H;
+            const float rs = (!GROUPED && ok) ? mt.s[0][r] : 1.0f;
+            const float v = group_sum<L>(acc[0][j][0]) * rs;
+            if ((lane % L) == 0 && ok) a.pout[(int64_t)pair * ex.H + r] = v;
+          }
+        });
+  }
+}
+
+// blocks per distinct expert for the pipelined kernels
+inline int v2_parts(int ntiles, int P, int max_blocks) {
+  const int cap = (max_blocks > 0 ? max_blocks : kV2MaxBlocks) / (P > 0 ? P : 1);
+  int parts = (ntiles + kWaves - 1) / kWaves;
+  if (parts > cap) parts = cap;
+  return parts < 1 ? 1 : parts;
+}
+
+template <int FMT, int XT, int L, int CB, bool GROUPED>
+inline hipError_t launch_gu_v2(const MoeDecodeArgs& a0, hipStream_t st) {
+  MoeDecodeArgs a = a0;
+  constexpr int RU = ru_for(2, CB);
+  const int P = a.T * a.topk;
+  const int kchunks = a.ex.H / Fmt<FMT>::kPerChunk;
+  const int ntiles = (a.ex.I + (64 / L) * RU - 1) / ((64 / L) * RU);
+  a.parts = v2_parts(ntiles, P, a.max_blocks);
+  a.segc = kchunks;
+  const size_t lds = stage_bytes(FMT, XT, 1, kchunks);
+  hipLaunchKernelGGL((moe_gate_up_v2_kernel<FMT, XT, L, CB, GROUPED>), dim3(P * a.parts), dim3(kThreads), lds, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <int FMT, int L, int CB, bool GROUPED>
+inline hipError_t launch_dn_v2(const MoeDecodeArgs& a0, hipStream_t st) {
+  MoeDecodeArgs a = a0;
+  constexpr int RU = ru_for(1, CB);
+  const int P = a.T * a.topk;
+  const int kchunks = a.ex.I / Fmt<FMT>::kPerChunk;
+  const int ntiles = (a.ex.H + (64 / L) * RU - 1) / ((64 / L) * RU);
+  a.parts = v2_parts(ntiles, P, a.max_blocks);
+  a.segc = kchunks;
+  const size_t lds = stage_bytes(FMT, kF32, 1, kchunks);
+  hipLaunchKernelGGL((moe_down_v2_kernel<FMT, L, CB, GROUPED>), dim3(P * a.parts), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+#define QM_V2_SWITCH(LAUNCH, ...)                     \
+  switch (L) {                                        \
+    case 16: QM_V2_CB(LAUNCH, 16, __VA_ARGS__) break; \
+    case 32: QM_V2_CB(LAUNCH, 32, __VA_ARGS__) break; \
+    default: QM_V2_CB(LAUNCH, 64, __VA_ARGS__) break; \
+  }
+
+// true when the single-token pipelined kernels apply: one token, at least 16
+// lanes per row and the whole activation row fits the staging budget
+inline bool v2_ok(int T, int L, size_t stage) { return T == 1 && L >= 16 && stage <= (size_t)kLdsBudget; }
+
+template <int FMT, int XT, bool GROUPED>
+inline hipError_t dispatch_gate_up_v2(const MoeDecodeArgs& a, int L, int CB, hipStream_t st) {
+#define QM_V2_CB(LAUNCH, LL, ...)                                   \
+  switch (CB) {                                                     \
+    case 1: return LAUNCH<FMT, __VA_ARGS__ LL, 1, GROUPED>(a, st);  \
+    case 2: return LAUNCH<FMT, __VA_ARGS__ LL, 2, GROUPED>(a, st);  \
+    case 3: return LAUNCH<FMT, __VA_ARGS__ LL, 3, GROUPED>(a, st);  \
+    case 4: return LAUNCH<FMT, __VA_ARGS__ LL, 4, GROUPED>(a, st);  \
+    default: return LAUNCH<FMT, __VA_ARGS__ LL, 8, GROUPED>(a, st); \
+  }
+  QM_V2_SWITCH(launch_gu_v2, XT, )
+  return hipErrorInvalidValue;
+}
+
+template <int FMT, bool GROUPED>
+inline hipError_t dispatch_down_v2(const MoeDecodeArgs& a, int L, int CB, hipStream_t st) {
+  QM_V2_SWITCH(launch_dn_v2, )
+  return hipErrorInvalidValue;
+#undef QM_V2_CB
+}
+
 inline int decode_nb(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
 // Stage 1: h for every valid pair.  Batch slots per pass over an expert's
@@ -250,6 +426,8 @@ inline int decode_nb(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)
 template <int FMT, int XT, bool GROUPED>
 inline hipError_t dispatch_gate_up(const MoeDecodeArgs& a, hipStream_t st) {
   const int Lg = lanes_per_row(a.ex.H / Fmt<FMT>::kPerChunk);
+  if (v2_ok(a.T, Lg, stage_bytes(FMT, XT, 1, a.ex.H / Fmt<FMT>::kPerChunk)))
+    return dispatch_gate_up_v2<FMT, XT, GROUPED>(a, Lg, v2_cb(a.ex.H / Fmt<FMT>::kPerChunk, Lg), st);
 #define QM_GU(NB)                                                      \
   switch (Lg) {                                                        \
     case 8: return launch_dec<FMT, XT, 8, NB, GROUPED>(a, st);         \
@@ -271,6 +449,15 @@ template <int FMT, bool GROUPED>
 inline hipError_t dispatch_down(const MoeDecodeArgs& a, hipStream_t st) {
   const int Ld = lanes_per_row(a.ex.I / Fmt<FMT>::kPerChunk);
   hipError_t err;
+  if (v2_ok(a.T, Ld, stage_bytes(FMT, kF32, 1, a.ex.I / Fmt<FMT>::kPerChunk))) {
+    err = dispatch_down_v2<FMT, GROUPED>(a, Ld, v2_cb(a.ex.I / Fmt<FMT>::kPerChunk, Ld), st);
+    if (err != hipSuccess) return err;
+    const int64_t total = (int64_t)a.T * a.ex.H;
+    int blocks = (int)((total + 255) / 256);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
 #define QM_DN(NB)                                                      \
   switch (Ld) {                                                        \
     case 8: err = launch_down<FMT, 8, NB, GROUPED>(a, st); break;      \

@@ -47,10 +47,35 @@ size_t stage_bytes(int fmt, int xdt, int NB, int segc) {
   return (size_t)NB * segc * per;
 }
 
+int v2_cb(int kchunks, int L) {
+  const int c = (kchunks + L - 1) / L;
+  return c <= 4 ? c : 8;
+}
+
+int v2_blocks(int ntiles, int max_blocks) {
+  int b = (ntiles + kWaves - 1) / kWaves;
+  const int cap = max_blocks > 0 ? max_blocks : kV2MaxBlocks;
+  return b < cap ? b : cap;
+}
+
 hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a0, int NB, hipStream_t st) {
   GemvArgs a = a0;
   const int kchunks = a.k / (fmt == kFmtInt4 ? 32 : 16);
   const int L = lanes_per_row(kchunks);
+  // pipelined path: one bf16 token, whole x in LDS, at least 16 lanes per row
+  if (NB == 1 && xdt == kBF16 && L >= 16 && stage_bytes(fmt, xdt, 1, kchunks) <= (size_t)kLdsBudget) {
+    const int CB = v2_cb(kchunks, L);
+    const int M = 1;
+    const int RU = 8 / (M * CB) >= 8 ? 8 : (8 / (M * CB) >= 4 ? 4 : (8 / (M * CB) >= 2 ? 2 : 1));
+    const int tile_rows = (64 / L) * RU;
+    const int ntiles = (a.n + tile_rows - 1) / tile_rows;
+    const int blocks = v2_blocks(ntiles, a.max_blocks);
+    const size_t lds = stage_bytes(fmt, xdt, 1, kchunks);
+    a.segc = kchunks;
+    if (fmt == kFmtInt4)
+      return grouped ? qgemv_v2_i4_bf16_g(a, L, CB, blocks, lds, st) : qgemv_v2_i4_bf16_r(a, L, CB, blocks, lds, st);
+    return qgemv_v2_i8_bf16_r(a, L, CB, blocks, lds, st);
+  }
   a.segc = seg_chunks(fmt, xdt, NB, kchunks);
   const int tiles = (a.n + rows_per_unit(L, NB) - 1) / rows_per_unit(L, NB);
   if (a.rounds < 1) a.rounds = 1;

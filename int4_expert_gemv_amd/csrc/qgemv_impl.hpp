@@ -88,4 +88,66 @@ inline hipError_t launch_g(const GemvArgs& a, int L, int NB, int blocks, size_t 
   }
 }
 
+
+// Pipelined single-token GEMV: the whole x is staged once per block, each
+// wave walks its tiles (grid stride) with unit i+1's weights in flight while
+// unit i is computed, and the first unit's loads are issued before staging.
+template <int FMT, int XT, int L, int RU, int CB, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void qgemv_v2_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr bool SPLIT = (FMT == kFmtInt4 && XT == kF32);
+  constexpr int RPW = 64 / L;
+  constexpr int TILE = RPW * RU;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane / L;
+  const int kchunks = a.k / Fmt<FMT>::kPerChunk;
+  const int ntiles = (a.n + TILE - 1) / TILE;
+  const int npasses = (kchunks + L * CB - 1) / (L * CB);
+  const int tstride = gridDim.x * kWaves;
+  const int tile0 = blockIdx.x * kWaves + wave;
+  const Mats<1> mt = {{a.q}, {a.s}};
+  TileW<1, RU, CB> A, B;
+  if (tile0 < ntiles)
+    unit_load<FMT, L, 1, RU, CB, GROUPED>(A, mt, a.row_bytes, a.G, a.gshift, tile0 * TILE + lrow, RPW, a.n, kchunks,
+                                          0);
+  stage_x<FMT, XT, 1>(lds, a.x, a.ldx, [](int) { return 0; }, 0, kchunks);
+  __syncthreads();
+  pipeline_tiles<FMT, SPLIT, L, 1, RU, CB, 1, GROUPED>(
+      A, B, mt, a.row_bytes, a.G, a.gshift, a.n, kchunks, tile0, tstride, ntiles, npasses, lds,
+      [&](int tile, float (&acc)[1][RU][1]) {
+#pragma unroll
+        for (int j = 0; j < RU; ++j) {
+          const int r = tile * TILE + lrow + j * RPW;
+          const float rs = (!GROUPED && r < a.n) ? a.s[r] : 1.0f;
+          const float v = group_sum<L>(acc[0][j][0]);
+          if ((lane % L) == 0 && r < a.n) a.y[r] = GROUPED ? v : v * rs;
+        }
+      });
+}
+
+template <int FMT, int XT, int L, int CB, bool GROUPED>
+inline hipError_t launch_v2_cb(const GemvArgs& a, int blocks, size_t lds, hipStream_t st) {
+  constexpr int RU = (8 / CB) >= 1 ? (8 / CB >= 8 ? 8 : (8 / CB >= 4 ? 4 : (8 / CB >= 2 ? 2 : 1))) : 1;
+  hipLaunchKernelGGL((qgemv_v2_kernel<FMT, XT, L, RU, CB, GROUPED>), dim3(blocks), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int XT, bool GROUPED>
+inline hipError_t launch_v2(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st) {
+#define QM_V2L(LL)                                                              \
+  switch (CB) {                                                                 \
+    case 1: return launch_v2_cb<FMT, XT, LL, 1, GROUPED>(a, blocks, lds, st);   \
+    case 2: return launch_v2_cb<FMT, XT, LL, 2, GROUPED>(a, blocks, lds, st);   \
+    case 3: return launch_v2_cb<FMT, XT, LL, 3, GROUPED>(a, blocks, lds, st);   \
+    case 4: return launch_v2_cb<FMT, XT, LL, 4, GROUPED>(a, blocks, lds, st);   \
+    default: return launch_v2_cb<FMT, XT, LL, 8, GROUPED>(a, blocks, lds, st);  \
+  }
+  switch (L) {
+    case 16: QM_V2L(16)
+    case 32: QM_V2L(32)
+    default: QM_V2L(64)
+  }
+#undef QM_V2L
+}
+
 }  // namespace qm
