@@ -492,6 +492,17 @@ __device__ __forceinline__ void pipeline_tiles(TileW<M, RU, CB>& a, TileW<M, RU,
 // Same LDS layout as stage_x, with the number of staged rows known only at
 // run time; XRow points at one staged row of that layout.
 
+// 16-byte slots of one staged row: 4 words x segc chunks, padded by 128 bytes
+// so that consecutive rows start on different LDS banks.
+__host__ __device__ constexpr int row_slots(int segc) { return 4 * segc + 8; }
+
+// LDS bytes of stage_rows for nrows rows of kchunks chunks
+template <int FMT, bool SPLIT>
+__host__ __device__ constexpr size_t stage_rows_bytes(int nrows, int kchunks) {
+  return (size_t)nrows * (FMT == kFmtInt4 ? (row_slots(kchunks) * 16 * (SPLIT ? 2 : 1) + kchunks * 4)
+                                          : row_slots(kchunks) * 16);
+}
+
 template <int FMT, int XT, typename TokF>
 __device__ __forceinline__ void stage_rows(char* __restrict__ lds, const void* __restrict__ x, int64_t ldx,
                                            TokF tok, int nrows, int kchunks) {
@@ -507,9 +518,10 @@ __device__ __forceinline__ void stage_rows(char* __restrict__ lds, const void* _
   constexpr int NV = (XT == kBF16) ? (WE + 7) / 8 : WE / 4;  // 16-byte loads per word (bf16 int8: half)
   constexpr int SB = 4;                             // words per thread in flight
   const int segc = kchunks;
+  const int rs = row_slots(segc);  // 16-byte slots per staged row, padded
   u32x4* hi = reinterpret_cast<u32x4*>(lds);
-  u32x4* lo = hi + nrows * 4 * segc;
-  float* off = reinterpret_cast<float*>(lds + (size_t)nrows * 4 * segc * 16 * (SPLIT ? 2 : 1));
+  u32x4* lo = hi + nrows * rs;
+  float* off = reinterpret_cast<float*>(lds + (size_t)nrows * rs * 16 * (SPLIT ? 2 : 1));
   const int total = nrows * segc * 4;
   for (int base = 0; base < total; base += kThreads * SB) {  // uniform trip count: DPP needs whole quads
     u32x4 raw[SB][NV];
@@ -570,14 +582,14 @@ __device__ __forceinline__ void stage_rows(char* __restrict__ lds, const void* _
         }
         sum = group_sum<4>(sum);  // the chunk's four words
         if (ok) {
-          hi[(b * 4 + j) * segc + c] = ph;
-          if constexpr (SPLIT) lo[(b * 4 + j) * segc + c] = pl;
+          hi[b * rs + j * segc + c] = ph;
+          if constexpr (SPLIT) lo[b * rs + j * segc + c] = pl;
           if (j == 0) off[b * segc + c] = -136.0f * sum;
         }
       } else {
         if (ok) {
           f32x4* q4 = reinterpret_cast<f32x4*>(lds);
-          q4[(b * 4 + j) * segc + c] = f32x4{v[0], v[1], v[2], v[3]};
+          q4[b * rs + j * segc + c] = f32x4{v[0], v[1], v[2], v[3]};
         }
       }
     }
@@ -594,10 +606,11 @@ struct XRow {
 template <int FMT, bool SPLIT>
 __device__ __forceinline__ XRow xrow(const char* lds, int nrows, int kchunks, int b) {
   XRow r;
+  const int rs = row_slots(kchunks);
   const u32x4* hi = reinterpret_cast<const u32x4*>(lds);
-  r.hi = hi + b * 4 * kchunks;
-  r.lo = hi + nrows * 4 * kchunks + b * 4 * kchunks;
-  r.off = reinterpret_cast<const float*>(lds + (size_t)nrows * 4 * kchunks * 16 * (SPLIT ? 2 : 1)) + b * kchunks;
+  r.hi = hi + b * rs;
+  r.lo = hi + nrows * rs + b * rs;
+  r.off = reinterpret_cast<const float*>(lds + (size_t)nrows * rs * 16 * (SPLIT ? 2 : 1)) + b * kchunks;
   r.segc = kchunks;
   return r;
 }

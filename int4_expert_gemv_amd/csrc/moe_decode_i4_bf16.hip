@@ -1,23 +1,23 @@
 // moe_decode_i4_bf16.hip -- instantiations of the MoE decode kernels for one (format,
 // activation type) pair.
-#include "moe_t1_impl.hpp"
+#include "moe_t1_lds.hpp"
 
 namespace qm {
 
 hipError_t moe_gate_up_i4_bf16_g(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_gate_up<kFmtInt4, kBF16, true>(a, st);
+  return stage_gate_up_any<kFmtInt4, kBF16, true>(a, st);
 }
 
 hipError_t moe_down_i4_g(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_down<kFmtInt4, true>(a, st);
+  return stage_down_any<kFmtInt4, true>(a, st);
 }
 
 hipError_t moe_gate_up_i4_bf16_r(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_gate_up<kFmtInt4, kBF16, false>(a, st);
+  return stage_gate_up_any<kFmtInt4, kBF16, false>(a, st);
 }
 
 hipError_t moe_down_i4_r(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_down<kFmtInt4, false>(a, st);
+  return stage_down_any<kFmtInt4, false>(a, st);
 }
 
 }  // namespace qm

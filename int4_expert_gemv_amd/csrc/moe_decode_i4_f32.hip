@@ -1,15 +1,15 @@
 // moe_decode_i4_f32.hip -- instantiations of the MoE decode kernels for one (format,
 // activation type) pair.
-#include "moe_t1_impl.hpp"
+#include "moe_t1_lds.hpp"
 
 namespace qm {
 
 hipError_t moe_gate_up_i4_f32_g(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_gate_up<kFmtInt4, kF32, true>(a, st);
+  return stage_gate_up_any<kFmtInt4, kF32, true>(a, st);
 }
 
 hipError_t moe_gate_up_i4_f32_r(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_gate_up<kFmtInt4, kF32, false>(a, st);
+  return stage_gate_up_any<kFmtInt4, kF32, false>(a, st);
 }
 
 }  // namespace qm

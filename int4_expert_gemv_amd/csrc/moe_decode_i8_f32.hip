@@ -1,11 +1,11 @@
 // moe_decode_i8_f32.hip -- instantiations of the MoE decode kernels for one (format,
 // activation type) pair.
-#include "moe_t1_impl.hpp"
+#include "moe_t1_lds.hpp"
 
 namespace qm {
 
 hipError_t moe_gate_up_i8_f32_r(const MoeDecodeArgs& a, hipStream_t st) {
-  return stage_gate_up<kFmtInt8, kF32, false>(a, st);
+  return stage_gate_up_any<kFmtInt8, kF32, false>(a, st);
 }
 
 }  // namespace qm

@@ -194,9 +194,10 @@ __global__ __launch_bounds__(kThreads) QM_T1_OCC void moe_down_t1_kernel(MoeDeco
     if (u[i] < nunits) load(buf[i], u[i]);
   stage_rows<FMT, kF32>(lds, a.h, ex.I, [&](int b) { return s_p[b]; }, np, kchunks);
   __syncthreads();
+  const int rs = row_slots(kchunks);
   const u32x4* hi = reinterpret_cast<const u32x4*>(lds);
-  const u32x4* lo = hi + np * 4 * kchunks;
-  const float* off = reinterpret_cast<const float*>(lds + (size_t)np * 4 * kchunks * 16 * (SPLIT ? 2 : 1));
+  const u32x4* lo = hi + np * rs;
+  const float* off = reinterpret_cast<const float*>(lds + (size_t)np * rs * 16 * (SPLIT ? 2 : 1));
   float acc[RU];
 #pragma unroll
   for (int j = 0; j < RU; ++j) acc[j] = 0.f;
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(kThreads) QM_T1_OCC void moe_down_t1_kernel(MoeDeco
           u32x4 xh[4], xl[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            xh[r] = hi[(q * 4 + r) * kchunks + c];
-            xl[r] = lo[(q * 4 + r) * kchunks + c];
+            xh[r] = hi[q * rs + r * kchunks + c];
+            xl[r] = lo[q * rs + r * kchunks + c];
           }
           const float xo = off[q * kchunks + c];
 #pragma unroll
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kThreads) QM_T1_OCC void moe_down_t1_kernel(MoeDeco
           const f32x4* xf = reinterpret_cast<const f32x4*>(lds);
           f32x4 xv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xv[r] = xf[(q * 4 + r) * kchunks + c];
+          for (int r = 0; r < 4; ++r) xv[r] = xf[q * rs + r * kchunks + c];
 #pragma unroll
           for (int j = 0; j < RU; ++j) {
             float s = 0.f;
@@ -293,7 +294,7 @@ inline hipError_t launch_gu_t1(const MoeDecodeArgs& a, hipStream_t st) {
   int blocks = (a.topk * ntiles + kWaves - 1) / kWaves;
   const int cap = a.max_blocks > 0 ? a.max_blocks : kV2MaxBlocks;
   if (blocks > cap) blocks = cap;
-  const size_t lds = stage_bytes(FMT, XT, 1, kchunks);
+  const size_t lds = stage_rows_bytes<FMT, FMT == kFmtInt4 && XT == kF32>(1, kchunks);
   if (kchunks == L * CB)
     hipLaunchKernelGGL((moe_gate_up_t1_kernel<FMT, XT, L, CB, GROUPED, true>), dim3(blocks), dim3(kThreads), lds,
                        st, a);
@@ -314,7 +315,7 @@ inline hipError_t launch_dn_t1(const MoeDecodeArgs& a, hipStream_t st) {
   int blocks = (ntiles + kWaves - 1) / kWaves;
   const int cap = a.max_blocks > 0 ? a.max_blocks : QM_T1_DOWN_BLOCKS;
   if (blocks > cap) blocks = cap;
-  const size_t lds = stage_bytes(FMT, kF32, a.topk, a.ex.I / Fmt<FMT>::kPerChunk);
+  const size_t lds = stage_rows_bytes<FMT, FMT == kFmtInt4>(a.topk, a.ex.I / Fmt<FMT>::kPerChunk);
   hipLaunchKernelGGL((moe_down_t1_kernel<FMT, CB, GROUPED>), dim3(blocks), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
@@ -352,7 +353,7 @@ template <int FMT, int XT, bool GROUPED>
 inline hipError_t stage_gate_up(const MoeDecodeArgs& a, hipStream_t st) {
   const int kch = a.ex.H / Fmt<FMT>::kPerChunk;
   const int L = lanes_per_row(kch);
-  if (t1_gate_up_ok(a.T, a.topk, L, kch, stage_bytes(FMT, XT, 1, kch)))
+  if (t1_gate_up_ok(a.T, a.topk, L, kch, stage_rows_bytes<FMT, FMT == kFmtInt4 && XT == kF32>(1, kch)))
     return dispatch_gate_up_t1<FMT, XT, GROUPED>(a, L, v2_cb(kch, L), st);
   return dispatch_gate_up<FMT, XT, GROUPED>(a, st);
 }
@@ -360,7 +361,8 @@ inline hipError_t stage_gate_up(const MoeDecodeArgs& a, hipStream_t st) {
 template <int FMT, bool GROUPED>
 inline hipError_t stage_down(const MoeDecodeArgs& a, hipStream_t st) {
   const int kch = a.ex.I / Fmt<FMT>::kPerChunk;
-  if (t1_down_ok(a.T, a.topk, stage_bytes(FMT, kF32, a.topk, kch))) return dispatch_down_t1<FMT, GROUPED>(a, st);
+  if (t1_down_ok(a.T, a.topk, stage_rows_bytes<FMT, FMT == kFmtInt4>(a.topk, kch)))
+    return dispatch_down_t1<FMT, GROUPED>(a, st);
   return dispatch_down<FMT, GROUPED>(a, st);
 }
 

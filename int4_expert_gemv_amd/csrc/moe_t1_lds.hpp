@@ -1,0 +1,504 @@
+// moe_t1_lds.hpp -- single-token routed expert FFN with the weight stream
+// prefetched into LDS (gfx950 global_load_lds_dwordx4 DMA).
+//
+// Computes what moe_t1_impl.hpp computes (the K-expert group of the colibri
+// page "Vulkan backend: expert tier + dense + MLA attention on any Vulkan 1.2
+// GPU": silu(gate x) * up x, then the down projection, outputs combined with
+// the routing weights).  The difference is where the prefetched weights wait:
+// every wave owns a ring of D slots in LDS; a slot holds one unit of work
+// (RU rows x CB 16-byte chunks per lane of every matrix, plus the matching
+// scales), filled by DMA loads that need no registers, and drained with one
+// ds_read_b128 per chunk right before the chunk is consumed.  D - 1 units
+// stay in flight while one is computed, at a register cost independent of D.
+//
+// vmcnt bookkeeping: a unit issues exactly U = 2 * (weight loads) VMEM
+// operations; before unit k is read the wave waits until at most
+// U * (units issued after k) VMEM operations are outstanding.  Anything else
+// issued after k (hidden-vector or output stores, staging loads) only makes
+// that wait stricter, never weaker.
+#pragma once
+#include "moe_t1_impl.hpp"
+
+namespace qm {
+
+#define QM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One lane's 16 bytes (or 4 bytes) into a wave-uniform LDS block of 1 KiB
+// (or 256 B) at lane-contiguous positions; non-temporal.
+__device__ __forceinline__ void dma16(const void* g, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, QM_LDS_PTR(lds_block), 16, 0, 2);
+}
+__device__ __forceinline__ void dma4(const void* g, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, QM_LDS_PTR(lds_block), 4, 0, 2);
+}
+
+// s_waitcnt vmcnt(N) with the other counters untouched (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | (((N >> 4) & 3) << 14));
+}
+
+// wait until at most n_after * U VMEM operations are outstanding (n_after < D)
+template <int U, int D>
+__device__ __forceinline__ void wait_units(int n_after) {
+  static_assert(D >= 1 && D <= 4, "ring depth");
+  if (n_after <= 0) {
+    wait_vmcnt<0>();
+  } else if (n_after == 1 || D <= 2) {
+    wait_vmcnt<U>();
+  } else if (n_after == 2 || D <= 3) {
+    wait_vmcnt<(2 * U < 64 ? 2 * U : 63)>();
+  } else {
+    wait_vmcnt<(3 * U < 64 ? 3 * U : 63)>();
+  }
+}
+
+// LDS reads of a slot must have returned before DMA refills it.
+__device__ __forceinline__ void slot_release() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  asm volatile("" ::: "memory");
+}
+
+constexpr size_t align_lds(size_t v) { return (v + 255) / 256 * 256; }
+
+template <int RU, int M, int CB>
+__host__ __device__ constexpr int ring_slot_bytes() {
+  return RU * M * CB * (1024 + 256);
+}
+
+// ---- gate + up ----------------------------------------------------------------
+// L = 64 lanes per row and exactly CB chunks per lane (H = 64 * CB * 32 for
+// int4).  Unit = RU consecutive rows of gate and up of one routed expert.
+template <int FMT, int XT, int CB, int RU, int D, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void moe_gate_up_t1l_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_e[kTopkMax];
+  constexpr bool SPLIT = (FMT == kFmtInt4 && XT == kF32);
+  constexpr int M = 2;
+  constexpr int NW = RU * M * CB;  // 1 KiB weight blocks per unit
+  constexpr int U = 2 * NW;        // VMEM operations per unit
+  constexpr int SLOT = ring_slot_bytes<RU, M, CB>();
+  const ExpertArgs& ex = a.ex;
+  const int k = a.topk;
+  if ((int)threadIdx.x < k) {
+    const int id = a.ids[threadIdx.x];
+    s_e[threadIdx.x] = (id >= 0 && id < ex.E) ? id : -1;
+  }
+  __syncthreads();
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int kchunks = 64 * CB;
+  const int ntiles = (ex.I + RU - 1) / RU;
+  const int nitems = k * ntiles;
+  const int istride = gridDim.x * kWaves;
+  char* ring = lds + align_lds(stage_rows_bytes<FMT, SPLIT>(1, kchunks)) + (size_t)wave * D * SLOT;
+  auto next_valid = [&](int it) {
+    while (it < nitems && uniform(s_e[it / ntiles]) < 0) it += istride;
+    return it;
+  };
+  auto issue = [&](int it, int slot) {
+    const int p = it / ntiles;
+    const int e = uniform(s_e[p]);
+    const int row0 = (it - p * ntiles) * RU;
+    char* sd = ring + slot * SLOT;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) {
+      const int r = min(row0 + j, ex.I - 1);  // a tail row past I reloads row I-1; its result is dropped
+      const int64_t er = (int64_t)e * ex.I + r;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint8_t* qrow = (m == 0 ? ex.gq : ex.uq) + er * ex.rb_h;
+        const float* srow = (m == 0 ? ex.gs : ex.us) + er * ex.G_h;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int c = lane + 64 * cb;
+          const int blk = (j * M + m) * CB + cb;
+          dma16(qrow + (int64_t)c * 16, sd + blk * 1024);
+          dma4(srow + (GROUPED ? (c >> ex.gshift) : 0), sd + NW * 1024 + blk * 256);
+        }
+      }
+    }
+  };
+  int head = next_valid(uniform(blockIdx.x * kWaves + wave));
+  int tail = head, inflight = 0;
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (tail < nitems) {
+      issue(tail, i);
+      ++inflight;
+      tail = next_valid(tail + istride);
+    }
+  stage_rows<FMT, XT>(lds, a.x, ex.H, [](int) { return 0; }, 1, kchunks);
+  __syncthreads();
+  const XRow xr = xrow<FMT, SPLIT>(lds, 1, kchunks, 0);
+  const NibConst nk = nib_const();
+  int hs = 0;
+  while (inflight > 0) {
+    wait_units<U, D>(inflight - 1);
+    const char* sd = ring + hs * SLOT;
+    float acc[M][RU];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < RU; ++j) acc[m][j] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+      u32x4 xh[4], xl[SPLIT ? 4 : 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xh[q] = xr.hi[q * kchunks + c];
+        if constexpr (SPLIT) xl[q] = xr.lo[q * kchunks + c];
+      }
+      const float xo = FMT == kFmtInt4 ? xr.off[c] : 0.f;
+#pragma unroll
+      for (int j = 0; j < RU; ++j)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int blk = (j * M + m) * CB + cb;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(sd + blk * 1024 + lane * 16);
+          const float s = *reinterpret_cast<const float*>(sd + NW * 1024 + blk * 256 + lane * 4);
+          float t;
+          if constexpr (FMT == kFmtInt4) {
+            t = xo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t pr[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pr[i] = nib_pair(w[q] >> (4 * i), nk);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t = dot2(pr[i], xh[q][i], t);
+              if constexpr (SPLIT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t = dot2(pr[i], xl[q][i], t);
+              }
+            }
+          } else {
+            const f32x4* xf = reinterpret_cast<const f32x4*>(xh);
+            t = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t = __builtin_fmaf((float)(int8_t)(w[q] >> (8 * i)), xf[q][i], t);
+          }
+          acc[m][j] = __builtin_fmaf(s, t, acc[m][j]);
+        }
+    }
+    slot_release();
+    const int it = head;
+    if (tail < nitems) {
+      issue(tail, hs);
+      tail = next_valid(tail + istride);
+    } else {
+      --inflight;
+    }
+    head = next_valid(head + istride);
+    hs = hs + 1 == D ? 0 : hs + 1;
+    const int p = it / ntiles, row0 = (it - p * ntiles) * RU;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) {
+      const float g = group_sum<64>(acc[0][j]);
+      const float v = group_sum<64>(acc[1][j]);
+      if (lane == 0 && row0 + j < ex.I) a.h[(int64_t)p * ex.I + row0 + j] = silu(g) * v;
+    }
+  }
+}
+
+// ---- down + weighted combine ----------------------------------------------------
+// Lanes are split into groups of LPP per routed pair (pair q = lane / LPP);
+// each lane walks chunks sub + LPP * i of its pair's row, so its expert and
+// routing weight stay fixed.  Unit = RU output rows x CB chunks per lane.
+template <int FMT, int CB, int RU, int D, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void moe_down_t1l_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_e[kTopkMax], s_p[kTopkMax], s_n;
+  __shared__ float s_w[kTopkMax];
+  constexpr bool SPLIT = (FMT == kFmtInt4);  // h is fp32
+  constexpr int M = 1;
+  constexpr int NW = RU * CB;
+  constexpr int U = 2 * NW;
+  constexpr int SLOT = ring_slot_bytes<RU, M, CB>();
+  const ExpertArgs& ex = a.ex;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int j = 0; j < a.topk; ++j) {
+      const int id = a.ids[j];
+      if (id >= 0 && id < ex.E) {
+        s_e[n] = id;
+        s_p[n] = j;
+        s_w[n] = a.w[j];
+        ++n;
+      }
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  const int np = s_n;
+  if (np == 0) {
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < ex.H; i += gridDim.x * kThreads) a.y[i] = 0.f;
+    return;
+  }
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int kchunks = ex.I / Fmt<FMT>::kPerChunk;
+  int npp = 1;
+  while (npp < np) npp <<= 1;
+  const int lpp = 64 / npp;             // lanes per pair (np <= 32 keeps lpp >= 2)
+  const int q = lane / lpp, sub = lane - q * lpp;
+  const bool lane_ok = q < np;
+  const int qq = lane_ok ? q : 0;
+  const int e = s_e[qq];
+  const float wq = lane_ok ? s_w[qq] : 0.f;
+  const int cpl = (kchunks + lpp - 1) / lpp;  // chunks per lane per row
+  const int npasses = (cpl + CB - 1) / CB;
+  const int ntiles = (ex.H + RU - 1) / RU;
+  const int nunits = ntiles * npasses;
+  const int ustride_t = gridDim.x * kWaves;  // tile stride
+  const size_t xbytes = align_lds(stage_rows_bytes<FMT, SPLIT>(a.topk, kchunks));
+  char* ring = lds + xbytes + (size_t)wave * D * SLOT;
+  auto next_unit = [&](int v) {
+    const int t = v / npasses, ps = v - t * npasses;
+    return ps + 1 < npasses ? v + 1 : (t + ustride_t) * npasses;
+  };
+  auto issue = [&](int v, int slot) {
+    const int t = v / npasses, ps = v - t * npasses;
+    char* sd = ring + slot * SLOT;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) {
+      const int r = min(t * RU + j, ex.H - 1);
+      const int64_t er = (int64_t)e * ex.H + r;
+      const uint8_t* qrow = ex.dq + er * ex.rb_i;
+      const float* srow = ex.ds + er * ex.G_i;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        int c = sub + lpp * (ps * CB + cb);
+        c = c < kchunks ? c : 0;  // past the row: reload chunk 0, weighted by zero below
+        const int blk = j * CB + cb;
+        dma16(qrow + (int64_t)c * 16, sd + blk * 1024);
+        dma4(srow + (GROUPED ? (c >> ex.gshift) : 0), sd + NW * 1024 + blk * 256);
+      }
+    }
+  };
+  int head = uniform(blockIdx.x * kWaves + wave) * npasses;
+  int tail = head, inflight = 0;
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (tail < nunits) {
+      issue(tail, i);
+      ++inflight;
+      tail = next_unit(tail);
+    }
+  stage_rows<FMT, kF32>(lds, a.h, ex.I, [&](int b) { return s_p[b]; }, np, kchunks);
+  __syncthreads();
+  const int rs = row_slots(kchunks);
+  const u32x4* xhi = reinterpret_cast<const u32x4*>(lds);
+  const u32x4* xlo = xhi + np * rs;
+  const float* xoff = reinterpret_cast<const float*>(lds + (size_t)np * rs * 16 * (SPLIT ? 2 : 1));
+  const f32x4* xf8 = reinterpret_cast<const f32x4*>(lds);
+  const NibConst nk = nib_const();
+  float acc[RU];
+#pragma unroll
+  for (int j = 0; j < RU; ++j) acc[j] = 0.f;
+  int hs = 0;
+  while (inflight > 0) {
+    wait_units<U, D>(inflight - 1);
+    const char* sd = ring + hs * SLOT;
+    const int v = head, t = v / npasses, ps = v - t * npasses;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c0 = sub + lpp * (ps * CB + cb);
+      const bool ok = lane_ok && c0 < kchunks;
+      const int c = ok ? c0 : 0;
+      const float mul = ok ? wq : 0.f;
+      if constexpr (FMT == kFmtInt4) {
+        u32x4 xh[4], xl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xh[r] = xhi[qq * rs + r * kchunks + c];
+          xl[r] = xlo[qq * rs + r * kchunks + c];
+        }
+        const float xo = xoff[qq * kchunks + c];
+#pragma unroll
+        for (int j = 0; j < RU; ++j) {
+          const int blk = j * CB + cb;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(sd + blk * 1024 + lane * 16);
+          const float s = *reinterpret_cast<const float*>(sd + NW * 1024 + blk * 256 + lane * 4);
+          float tt = xo;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint32_t pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = nib_pair(w[r] >> (4 * i), nk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tt = dot2(pr[i], xh[r][i], tt);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tt = dot2(pr[i], xl[r][i], tt);
+          }
+          acc[j] = __builtin_fmaf(mul * s, tt, acc[j]);
+        }
+      } else {
+        f32x4 xv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xv[r] = xf8[qq * rs + r * kchunks + c];
+#pragma unroll
+        for (int j = 0; j < RU; ++j) {
+          const int blk = j * CB + cb;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(sd + blk * 1024 + lane * 16);
+          const float s = *reinterpret_cast<const float*>(sd + NW * 1024 + blk * 256 + lane * 4);
+          float tt = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tt = __builtin_fmaf((float)(int8_t)(w[r] >> (8 * i)), xv[r][i], tt);
+          acc[j] = __builtin_fmaf(mul * s, tt, acc[j]);
+        }
+      }
+    }
+    slot_release();
+    if (tail < nunits) {
+      issue(tail, hs);
+      tail = next_unit(tail);
+    } else {
+      --inflight;
+    }
+    head = next_unit(head);
+    hs = hs + 1 == D ? 0 : hs + 1;
+    if (ps == npasses - 1) {
+#pragma unroll
+      for (int j = 0; j < RU; ++j) {
+        const float yv = group_sum<64>(acc[j]);
+        if (lane == 0 && t * RU + j < ex.H) a.y[t * RU + j] = yv;
+        acc[j] = 0.f;
+      }
+    }
+  }
+}
+
+// ---- launch ---------------------------------------------------------------------
+
+#ifndef QM_LDS_GU_D
+#define QM_LDS_GU_D 2
+#endif
+#ifndef QM_LDS_DN_D
+#define QM_LDS_DN_D 2
+#endif
+#ifndef QM_LDS_GU_BLOCKS
+#define QM_LDS_GU_BLOCKS 512
+#endif
+#ifndef QM_LDS_DN_BLOCKS
+#define QM_LDS_DN_BLOCKS 256
+#endif
+constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
+
+template <int CB>
+constexpr int gu_ru() { return CB >= 3 ? 1 : (CB == 2 ? 1 : 2); }
+
+template <int FMT, int XT, int CB, bool GROUPED>
+inline size_t gu_lds_bytes() {
+  return align_lds(stage_rows_bytes<FMT, FMT == kFmtInt4 && XT == kF32>(1, 64 * CB)) +
+         (size_t)kWaves * QM_LDS_GU_D * ring_slot_bytes<gu_ru<CB>(), 2, CB>();
+}
+
+template <int FMT, int XT, int CB, bool GROUPED>
+inline hipError_t launch_gu_t1l(const MoeDecodeArgs& a, hipStream_t st) {
+  constexpr int RU = gu_ru<CB>();
+  const int ntiles = (a.ex.I + RU - 1) / RU;
+  int blocks = (a.topk * ntiles + kWaves - 1) / kWaves;
+  const int cap = a.max_blocks > 0 ? a.max_blocks : QM_LDS_GU_BLOCKS;
+  if (blocks > cap) blocks = cap;
+  const size_t lds = gu_lds_bytes<FMT, XT, CB, GROUPED>();
+  hipLaunchKernelGGL((moe_gate_up_t1l_kernel<FMT, XT, CB, RU, QM_LDS_GU_D, GROUPED>), dim3(blocks), dim3(kThreads),
+                     lds, st, a);
+  return hipGetLastError();
+}
+
+constexpr int kDnRU = 2;
+
+template <int FMT, int CB>
+inline size_t dn_lds_bytes(int topk, int kchunks) {
+  return align_lds(stage_rows_bytes<FMT, FMT == kFmtInt4>(topk, kchunks)) +
+         (size_t)kWaves * QM_LDS_DN_D * ring_slot_bytes<kDnRU, 1, CB>();
+}
+
+template <int FMT, int CB, bool GROUPED>
+inline hipError_t launch_dn_t1l(const MoeDecodeArgs& a, hipStream_t st) {
+  const int ntiles = (a.ex.H + kDnRU - 1) / kDnRU;
+  int blocks = (ntiles + kWaves - 1) / kWaves;
+  const int cap = a.max_blocks > 0 ? a.max_blocks : QM_LDS_DN_BLOCKS;
+  if (blocks > cap) blocks = cap;
+  const size_t lds = dn_lds_bytes<FMT, CB>(a.topk, a.ex.I / Fmt<FMT>::kPerChunk);
+  hipLaunchKernelGGL((moe_down_t1l_kernel<FMT, CB, kDnRU, QM_LDS_DN_D, GROUPED>), dim3(blocks), dim3(kThreads), lds,
+                     st, a);
+  return hipGetLastError();
+}
+
+// The LDS-ring gate+up kernel needs H to be exactly 64 * CB chunks (CB <= 4);
+// both need T = 1 and their LDS within the workgroup limit.
+template <int FMT, int XT, bool GROUPED>
+inline bool try_gate_up_t1l(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err) {
+  if (a.T != 1 || a.topk > kTopkMax) return false;
+  const int kch = a.ex.H / Fmt<FMT>::kPerChunk;
+  if (kch % 64 || kch / 64 > 4 || kch / 64 < 1) return false;
+  switch (kch / 64) {
+    case 1:
+      if (gu_lds_bytes<FMT, XT, 1, GROUPED>() > (size_t)kLdsMax) return false;
+      *err = launch_gu_t1l<FMT, XT, 1, GROUPED>(a, st);
+      return true;
+    case 2:
+      if (gu_lds_bytes<FMT, XT, 2, GROUPED>() > (size_t)kLdsMax) return false;
+      *err = launch_gu_t1l<FMT, XT, 2, GROUPED>(a, st);
+      return true;
+    case 3:
+      if (gu_lds_bytes<FMT, XT, 3, GROUPED>() > (size_t)kLdsMax) return false;
+      *err = launch_gu_t1l<FMT, XT, 3, GROUPED>(a, st);
+      return true;
+    default:
+      if (gu_lds_bytes<FMT, XT, 4, GROUPED>() > (size_t)kLdsMax) return false;
+      *err = launch_gu_t1l<FMT, XT, 4, GROUPED>(a, st);
+      return true;
+  }
+}
+
+// chunks per lane and pass: the chunks one lane owns in a row when every
+// routed pair is valid (lanes per pair = 64 / next_pow2(top_k)), up to 4
+template <int FMT, bool GROUPED>
+inline bool try_down_t1l(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err) {
+  if (a.T != 1 || a.topk > kTopkMax) return false;
+  const int kch = a.ex.I / Fmt<FMT>::kPerChunk;
+  int npp = 1;
+  while (npp < a.topk) npp <<= 1;
+#ifndef QM_LDS_DN_CBMAX
+#define QM_LDS_DN_CBMAX 4
+#endif
+  int cpl = (kch + 64 / npp - 1) / (64 / npp);
+  if (cpl > QM_LDS_DN_CBMAX) cpl = QM_LDS_DN_CBMAX;
+  if (cpl <= 1) {
+    if (dn_lds_bytes<FMT, 1>(a.topk, kch) > (size_t)kLdsMax) return false;
+    *err = launch_dn_t1l<FMT, 1, GROUPED>(a, st);
+  } else if (cpl == 2) {
+    if (dn_lds_bytes<FMT, 2>(a.topk, kch) > (size_t)kLdsMax) return false;
+    *err = launch_dn_t1l<FMT, 2, GROUPED>(a, st);
+  } else {
+    if (dn_lds_bytes<FMT, 4>(a.topk, kch) > (size_t)kLdsMax) return false;
+    *err = launch_dn_t1l<FMT, 4, GROUPED>(a, st);
+  }
+  return true;
+}
+
+// Stage entry points used by the C ABI: LDS-ring kernels first, then the
+// register-pipelined single-token kernels, then the general decode kernels.
+template <int FMT, int XT, bool GROUPED>
+inline hipError_t stage_gate_up_any(const MoeDecodeArgs& a, hipStream_t st) {
+  hipError_t err = hipSuccess;
+  if (try_gate_up_t1l<FMT, XT, GROUPED>(a, st, &err)) return err;
+  return stage_gate_up<FMT, XT, GROUPED>(a, st);
+}
+
+template <int FMT, bool GROUPED>
+inline hipError_t stage_down_any(const MoeDecodeArgs& a, hipStream_t st) {
+  hipError_t err = hipSuccess;
+  if (try_down_t1l<FMT, GROUPED>(a, st, &err)) return err;
+  return stage_down<FMT, GROUPED>(a, st);
+}
+
+}  // namespace qm

@@ -4,7 +4,7 @@
 // call; a rejected call enqueues nothing and writes nothing (the colibri page
 // "qwen36: Vulkan expert tier, and staged device-local uploads" keeps the
 // caller's output untouched when the GPU path refuses a request).
-#include "../../include/qmoe.h"
+#include "qmoe.h"
 #include "launch.hpp"
 
 #include <limits.h>
