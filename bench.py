@@ -66,6 +66,26 @@ def expert_bytes(fmt, H, I, gs):
     return 2 * I * (H + 4) + H * (I + 4)
 
 
+def counter_traffic(name):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<name>.txt: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled
+    by the factor a plain 1 GiB copy gives), or None when the summary is
+    missing or was taken from other kernel sources than the ones built now."""
+    from int4_expert_gemv_amd import build as hipbuild
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_digest") != hipbuild.source_digest() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
 def routing_schedule(seed, n_steps, T, E, k):
     """Per step: T tokens' top-k ids (distinct within a token) taken from a
     walk over random permutations of the experts, and softmax gate weights."""
@@ -161,6 +181,7 @@ def bench_moe(args, E, H, I):
                          "%.2f ms per step" % (done, done - 1, 1e3 * el / max(done, 1))}
 
     gname = "g%d" % gs if gs else "row"
+    tag = "%s_%s_t%d" % (args.config, gname, T)
     return {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_layer": round(ms_step * 1e3, 3),
@@ -170,8 +191,9 @@ def bench_moe(args, E, H, I):
                    "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": "int4-" + gname,
                    "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "moe_gate_up_kernel (fused gate+up+SiLU)", "us_per_launch": round(gu_ms * 1e3, 3),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("moe_gate_up_%s_counters" % tag),
+                     "kernel": "fused gate+up+SiLU (moe_gate_up stage)", "us_per_launch": round(gu_ms * 1e3, 3),
                      "bytes_per_launch": int(gu_bytes)},
         "parity": {"max_norm_err": err, "tol": 2e-4, "stage_entry_points_identical": same},
         "cpu_baseline": cpu,

@@ -26,6 +26,22 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def source_digest():
+    """sha256 over every kernel source, header and the public header (in name
+    order): a hardware-counter summary taken from a build is valid only while
+    this digest is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(FLAGS[:-2]).encode())
+    return h.hexdigest()[:16]
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", "-o", obj, src]
