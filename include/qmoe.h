@@ -115,7 +115,7 @@ QM_API int qgemm_small(const qm_qmat *w, const void *x, int32_t x_dtype, int32_t
                 float *y, int64_t ldy, void *stream);
 
 /* Bytes of device workspace moe_expert_ffn needs for these sizes (covers
- * both kernel paths when n_tokens <= QM_DECODE_MAX_TOKENS).  0 on invalid
+ * every kernel path moe_expert_ffn_path may take for them).  0 on invalid
  * arguments. */
 QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, int32_t top_k);
 
@@ -135,14 +135,19 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  *            256-byte aligned; its contents are scratch (not preserved).
  * n_tokens <= QM_DECODE_MAX_TOKENS runs the decode kernels (fp32 hidden
  * vector); larger batches run the expert-grouped prefill kernels (bf16 MFMA,
- * hidden vector and fp32 activations rounded to bf16).                     */
+ * hidden vector and fp32 activations rounded to bf16) when the experts
+ * qualify -- int4 with a group size (or, per row, a row length) that is a
+ * multiple of 64, at most 128 groups per row, hidden % 512 == 0,
+ * inter % 256 == 0, n_experts <= 8192 -- and otherwise the decode kernels
+ * QM_DECODE_MAX_TOKENS tokens at a time.                                   */
 QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
                    const int32_t *topk_ids, const float *topk_w, int32_t top_k,
                    float *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_expert_ffn with the kernel path chosen by the caller: QM_PATH_AUTO,
- * QM_PATH_DECODE (needs n_tokens <= QM_DECODE_MAX_TOKENS) or
- * QM_PATH_PREFILL (any n_tokens).                                          */
+ * QM_PATH_DECODE (any n_tokens, QM_DECODE_MAX_TOKENS per pass) or
+ * QM_PATH_PREFILL (any n_tokens; QM_ERR_UNSUPPORTED for experts the
+ * prefill kernels do not take, see moe_expert_ffn).                        */
 QM_API int moe_expert_ffn_path(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
                         const int32_t *topk_ids, const float *topk_w, int32_t top_k,
                         float *y, void *workspace, size_t workspace_bytes, void *stream,

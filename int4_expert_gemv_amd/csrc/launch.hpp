@@ -93,11 +93,12 @@ QM_DECL_MOE(moe_down_i8_r)
 hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 
-// moe_prefill.hip
-struct MoePrefillArgs;
-size_t moe_prefill_workspace(int T, int topk, int E, int H, int I);
-hipError_t launch_moe_prefill(int fmt, int xdt, bool grouped, const ExpertArgs& ex, const void* x,
-                              const int32_t* ids, const float* w, int T, int topk, float* y, void* ws,
-                              hipStream_t st);
+// moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
+// (or row length, per-row scales) is a multiple of 64 with at most 128 groups
+// per row, hidden % 512 == 0, inter % 256 == 0 and at most 8192 experts.
+bool moe_prefill_supported(int fmt, int topk, const ExpertArgs& e);
+size_t moe_prefill_workspace(int T, int topk, const ExpertArgs& e);
+hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void* x, const int32_t* ids,
+                              const float* w, int T, int topk, float* y, void* ws, hipStream_t st);
 
 }  // namespace qm

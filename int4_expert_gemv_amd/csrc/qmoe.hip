@@ -95,6 +95,15 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
 
 // ---- MoE -------------------------------------------------------------------------
 
+// Shapes, format and group size only (no pointers).
+bool moe_shape_ok(const qm_experts* ex) {
+  if (ex->n_experts < 1 || ex->hidden < 1 || ex->inter < 1) return false;
+  if (check_shape(ex->fmt, ex->inter, ex->hidden, ex->group_size) != QM_OK) return false;
+  if (check_shape(ex->fmt, ex->hidden, ex->inter, ex->group_size) != QM_OK) return false;
+  const int gh = eff_gs(ex->fmt, ex->group_size, ex->hidden);
+  const int gi = eff_gs(ex->fmt, ex->group_size, ex->inter);
+  return (gh == 0) == (gi == 0);
+}
 int check_experts(const qm_experts* ex) {
   if (!ex) return QM_ERR_INVALID;
   if (ex->n_experts < 1 || ex->hidden < 0 || ex->inter < 0) return QM_ERR_INVALID;
@@ -193,14 +202,17 @@ int qgemm_small(const qm_qmat* w, const void* x, int32_t x_dtype, int32_t batch,
 size_t moe_expert_ffn_workspace(const qm_experts* ex, int32_t n_tokens, int32_t top_k) {
   if (!ex || n_tokens < 0 || top_k < 1 || top_k > QM_TOPK_MAX) return 0;
   if (ex->hidden < 1 || ex->inter < 1 || ex->n_experts < 1) return 0;
-  size_t need = moe_prefill_workspace(n_tokens, top_k, ex->n_experts, ex->hidden, ex->inter);
-  if (n_tokens <= QM_DECODE_MAX_TOKENS) {
-    const size_t d = decode_workspace(n_tokens, top_k, ex->hidden, ex->inter);
-    if (d > need) need = d;
+  const int td = n_tokens < QM_DECODE_MAX_TOKENS ? n_tokens : QM_DECODE_MAX_TOKENS;
+  size_t need = decode_workspace(td, top_k, ex->hidden, ex->inter);
+  if (moe_shape_ok(ex)) {
+    const ExpertArgs e = expert_args(ex);
+    if (moe_prefill_supported(ex->fmt, top_k, e)) {
+      const size_t p = moe_prefill_workspace(n_tokens, top_k, e);
+      if (p > need) need = p;
+    }
   }
   return need < 256 ? 256 : need;
 }
-
 int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens,
                         const int32_t* topk_ids, const float* topk_w, int32_t top_k, float* y, void* workspace,
                         size_t workspace_bytes, void* stream, int32_t path) {
@@ -214,29 +226,37 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
-  if (path == QM_PATH_AUTO) path = n_tokens <= QM_DECODE_MAX_TOKENS ? QM_PATH_DECODE : QM_PATH_PREFILL;
-  if (path == QM_PATH_DECODE && n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
+  const bool pre_ok = moe_prefill_supported(ex->fmt, top_k, expert_args(ex));
+  if (path == QM_PATH_AUTO)
+    path = (n_tokens > QM_DECODE_MAX_TOKENS && pre_ok) ? QM_PATH_PREFILL : QM_PATH_DECODE;
+  if (path == QM_PATH_PREFILL && !pre_ok) return QM_ERR_UNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) ||
       workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ExpertArgs e = expert_args(ex);
-  hipError_t err;
-  if (path == QM_PATH_DECODE) {
-    MoeDecodeArgs a = decode_args(e, x, n_tokens, topk_ids, topk_w, top_k, y, workspace);
-    err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
-    if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
+  hipError_t err = hipSuccess;
+  if (path == QM_PATH_PREFILL) {
+    err = launch_moe_prefill(ex->fmt, x_dtype, e, x, topk_ids, topk_w, n_tokens, top_k, y, workspace, s);
   } else {
-    err = launch_moe_prefill(ex->fmt, x_dtype, grouped, e, x, topk_ids, topk_w, n_tokens, top_k, y, workspace, s);
+    // decode kernels, QM_DECODE_MAX_TOKENS tokens per pass (one pass for a decode batch)
+    const size_t xs = (size_t)ex->hidden * xsize(x_dtype);
+    for (int t0 = 0; t0 < n_tokens && err == hipSuccess; t0 += QM_DECODE_MAX_TOKENS) {
+      const int nt = n_tokens - t0 < QM_DECODE_MAX_TOKENS ? n_tokens - t0 : QM_DECODE_MAX_TOKENS;
+      MoeDecodeArgs a = decode_args(e, static_cast<const char*>(x) + (size_t)t0 * xs, nt,
+                                    topk_ids + (size_t)t0 * top_k, topk_w + (size_t)t0 * top_k, top_k,
+                                    y + (size_t)t0 * ex->hidden, workspace);
+      err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
+      if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
+    }
   }
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
-
 int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_ids,
                 int32_t top_k, float* h, void* stream) {
   if (x_dtype != QM_F32 && x_dtype != QM_BF16) return QM_ERR_INVALID;

@@ -129,7 +129,10 @@ def test_moe_rejects(q):
     assert _moe(q, _experts(q), k=33) == -2                  # top_k above QM_TOPK_MAX
     assert _moe(q, _experts(q, H=250)) == -2                 # hidden not a multiple of 32
     assert _moe(q, _experts(q, gate_q=FAKE + 4)) == -2       # misaligned weights
-    assert _moe(q, _experts(q), T=9, path=1) == -2           # decode path above QM_DECODE_MAX_TOKENS
+    assert _moe(q, _experts(q, fmt=1, gs=0), T=16, path=2) == -2   # prefill kernels: int4 only
+    assert _moe(q, _experts(q, gs=32), T=16, path=2) == -2         # prefill kernels: group size >= 64
+    assert _moe(q, _experts(q, H=288, gs=0), T=16, path=2) == -2   # prefill kernels: hidden % 512
+    assert _moe(q, _experts(q, H=512, I=160, gs=0), T=16, path=2) == -2   # prefill kernels: inter % 256
     assert _moe(q, _experts(q, H=256, I=96, gs=64)) == -2    # I=96 with g64: ragged group
     assert _moe(q, _experts(q), ws_bytes=16) == -3           # workspace too small
     assert _moe(q, _experts(q), ws=0) == -3                  # no workspace
@@ -145,5 +148,12 @@ def test_workspace_sizes(q):
     w1 = q.lib.moe_expert_ffn_workspace(ctypes.byref(ex), 1, 8)
     w8 = q.lib.moe_expert_ffn_workspace(ctypes.byref(ex), 8, 8)
     assert w1 >= 8 * (2048 + 6144) * 4 and w8 >= 64 * (2048 + 6144) * 4 and w8 > w1
+    # the 512-token batch-union: per-pair outputs alone are 4096 x 6144 fp32
+    w512 = q.lib.moe_expert_ffn_workspace(ctypes.byref(_experts(q, E=256, H=6144, I=2048)), 512, 8)
+    assert w512 >= 4096 * 6144 * 4 + 4096 * 2048 * 2 + 512 * 6144 * 2
+    # int8 experts never take the prefill kernels: a large batch needs one decode pass of 8 tokens
+    ex8 = _experts(q, E=320, H=6144, I=2048, fmt=1, gs=0)
+    assert q.lib.moe_expert_ffn_workspace(ctypes.byref(ex8), 512, 8) == \
+        q.lib.moe_expert_ffn_workspace(ctypes.byref(ex8), 8, 8)
     assert q.lib.moe_expert_ffn_workspace(ctypes.byref(ex), 1, 0) == 0
     assert q.lib.moe_expert_ffn_workspace(None, 1, 8) == 0
