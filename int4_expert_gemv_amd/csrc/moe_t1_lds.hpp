@@ -374,6 +374,175 @@ __global__ __launch_bounds__(kThreads) void moe_down_t1l_kernel(MoeDecodeArgs a)
   }
 }
 
+
+// ---- down + weighted combine, hidden vector in registers ----------------------
+// One wave owns PPW = 64 / L routed pairs (L lanes each) and, for a slice of
+// this block's output rows, reads every row of those pairs' down matrices:
+// lane (pair, sub) holds chunks c = sub + L * i (i < CPL) of the row, and
+// those chunks of h sit in its registers for the whole kernel (converted once
+// to bf16 hi/lo pairs plus the chunk's -136 * sum offset), so the LDS holds
+// only the weight ring.  Unit = one row of the wave's pairs; the ring keeps
+// D - 1 units in flight per wave.  Each lane stores its weighted partial of a
+// row in a per-wave LDS table (no cross-lane work inside the loop); at the
+// end every row's 64 partials of every pair group are added in a fixed order
+// (lane order within a group, then group order), so y is written once,
+// deterministically.
+constexpr int kDW = 8;           // waves per block of the register-h down kernel
+constexpr int kDT = 64 * kDW;
+
+// wait until at most n * U VMEM operations are outstanding (0 <= n <= N)
+template <int U, int N>
+__device__ __forceinline__ void wait_units_upto(int n) {
+  if constexpr (N <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<(N * U < 64 ? N * U : 63)>();
+    else
+      wait_units_upto<U, N - 1>(n);
+  }
+}
+
+template <int FMT, int L, int CPL, int D, bool GROUPED>
+__global__ __launch_bounds__(kDT) void moe_down_t1r_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_e[kTopkMax], s_p[kTopkMax], s_n;
+  __shared__ float s_w[kTopkMax];
+  constexpr int PPW = 64 / L;
+  constexpr int U = 2 * CPL;  // VMEM operations per unit
+  constexpr int SLOT = ring_slot_bytes<1, 1, CPL>();
+  constexpr int PER = Fmt<FMT>::kPerChunk;
+  const ExpertArgs& ex = a.ex;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int j = 0; j < a.topk; ++j) {
+      const int id = a.ids[j];
+      if (id >= 0 && id < ex.E) {
+        s_e[n] = id;
+        s_p[n] = j;
+        s_w[n] = a.w[j];
+        ++n;
+      }
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  const int np = s_n;
+  const int npg = (np + PPW - 1) / PPW;  // pair groups: waves per row slice
+  int npg2 = 1;
+  while (npg2 < npg) npg2 <<= 1;  // <= kDW (checked on the host for top_k)
+  const int S = kDW / npg2;       // row slices per block
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int pg = wave % npg2, sl = wave / npg2;
+  const int qi = lane / L, sub = lane - qi * L;
+  const int q = pg * PPW + qi;
+  const bool qok = pg < npg && q < np;
+  const int qq = qok ? q : 0;
+  const int e = s_e[qq], prow = s_p[qq];
+  const float wq = qok ? s_w[qq] : 0.f;
+  const int R = (ex.H + gridDim.x - 1) / gridDim.x;
+  const int r0 = blockIdx.x * R, r1 = min(ex.H, r0 + R);
+  float* part = reinterpret_cast<float*>(lds + (size_t)kDW * D * SLOT);  // [R][kDW][64] lane partials
+  char* ring = lds + (size_t)wave * D * SLOT;
+  const int span = r1 - r0 - sl;
+  const int nunits = (pg < npg && span > 0) ? (span + S - 1) / S : 0;  // wave-uniform
+  auto issue = [&](int u, int slot) {
+    const int r = r0 + sl + S * u;
+    const int64_t er = (int64_t)e * ex.H + r;
+    const uint8_t* qrow = ex.dq + er * ex.rb_i;
+    const float* srow = ex.ds + er * ex.G_i;
+    char* sd = ring + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = sub + L * i;
+      dma16(qrow + (int64_t)c * 16, sd + i * 1024);
+      dma4(srow + (GROUPED ? (c >> ex.gshift) : 0), sd + CPL * 1024 + i * 256);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (u < nunits) issue(u, u);
+
+  // this lane's chunks of h, in registers
+  const float* hrow = a.h + (int64_t)prow * ex.I;
+  u32x4 hh[CPL][4], hl[CPL][4];
+  float ho[CPL];
+  f32x4 hf[CPL][4];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = sub + L * i;
+    if constexpr (FMT == kFmtInt4) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 va = *reinterpret_cast<const f32x4*>(hrow + c * 32 + 8 * j);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(hrow + c * 32 + 8 * j + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x0 = qok ? va[t] : 0.f, x1 = qok ? vb[t] : 0.f;
+          const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+          const float r0f = x0 - bf16_bits_to_f32(h0), r1f = x1 - bf16_bits_to_f32(h1);
+          const uint32_t l0 = f32_to_bf16_bits(r0f), l1 = f32_to_bf16_bits(r1f);
+          hh[i][j][t] = h0 | (h1 << 16);
+          hl[i][j][t] = l0 | (l1 << 16);
+          sum += (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
+        }
+      }
+      ho[i] = -136.0f * sum;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(hrow + c * 16 + 4 * j);
+        hf[i][j] = qok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  const NibConst nk = nib_const();
+  for (int u = 0; u < nunits; ++u) {
+    wait_units_upto<U, D - 2>(min(D - 2, nunits - 1 - u));
+    const char* sd = ring + (u % D) * SLOT;
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(sd + i * 1024 + lane * 16);
+      const float sc = *reinterpret_cast<const float*>(sd + CPL * 1024 + i * 256 + lane * 4);
+      float tt;
+      if constexpr (FMT == kFmtInt4) {
+        tt = ho[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t pr[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) pr[m] = nib_pair(w[j] >> (4 * m), nk);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) tt = dot2(pr[m], hh[i][j][m], tt);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) tt = dot2(pr[m], hl[i][j][m], tt);
+        }
+      } else {
+        tt = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) tt = __builtin_fmaf((float)(int8_t)(w[j] >> (8 * m)), hf[i][j][m], tt);
+      }
+      t = __builtin_fmaf(sc, tt, t);
+    }
+    slot_release();
+    if (u + D - 1 < nunits) issue(u + D - 1, (u + D - 1) % D);
+    part[((sl + S * u) * kDW + pg) * 64 + lane] = wq * t;
+  }
+  __syncthreads();
+  // row i of this block: one wave per row, lanes add the pair groups' partials
+  for (int i = wave; i < r1 - r0; i += kDW) {
+    float v = 0.f;
+    for (int g = 0; g < npg; ++g) v += part[(i * kDW + g) * 64 + lane];
+    v = group_sum<64>(v);
+    if (lane == 0) a.y[r0 + i] = v;
+  }
+  (void)PER;
+}
+
 // ---- launch ---------------------------------------------------------------------
 
 #ifndef QM_LDS_GU_D
@@ -485,6 +654,61 @@ inline bool try_down_t1l(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err
   return true;
 }
 
+
+#ifndef QM_DOWN_REG
+#define QM_DOWN_REG 1
+#endif
+#ifndef QM_DOWN_REG_BLOCKS
+#define QM_DOWN_REG_BLOCKS 512
+#endif
+#ifndef QM_DOWN_REG_D
+#define QM_DOWN_REG_D 4
+#endif
+
+template <int FMT, int L, int CPL, bool GROUPED>
+inline hipError_t launch_dn_t1r(const MoeDecodeArgs& a, hipStream_t st) {
+  constexpr int D = CPL == 1 ? QM_DOWN_REG_D : (QM_DOWN_REG_D + 1) / 2;
+  constexpr int PPW = 64 / L;
+  const int npg = (a.topk + PPW - 1) / PPW;
+  int npg2 = 1;
+  while (npg2 < npg) npg2 <<= 1;
+  const int S = kDW / npg2;
+  int blocks = a.max_blocks > 0 ? a.max_blocks : QM_DOWN_REG_BLOCKS;
+  if (blocks > (a.ex.H + S - 1) / S) blocks = (a.ex.H + S - 1) / S;
+  const int R = (a.ex.H + blocks - 1) / blocks;
+  const size_t lds = (size_t)kDW * D * ring_slot_bytes<1, 1, CPL>() + (size_t)R * kDW * 64 * 4;
+  if (lds > (size_t)kLdsMax) return hipErrorNotSupported;
+  hipLaunchKernelGGL((moe_down_t1r_kernel<FMT, L, CPL, D, GROUPED>), dim3(blocks), dim3(kDT), lds, st, a);
+  return hipGetLastError();
+}
+
+// Register-h down kernel: T = 1, each row's chunks over 64 lanes with one or
+// two chunks per lane (one wave per routed pair), at most kDW pairs.
+template <int FMT, bool GROUPED>
+inline bool try_down_t1r(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err) {
+  if (!QM_DOWN_REG || a.T != 1 || a.topk > kTopkMax) return false;
+  const int kch = a.ex.I / Fmt<FMT>::kPerChunk;
+  int L = 0, cpl = 0;
+  // Short rows (fewer than 64 chunks) finish faster in the shared-LDS kernel,
+  // whose startup is shorter; the register-h kernel takes rows of 64 or 128
+  // chunks (inter 2048 / 4096 for int4).
+  if (kch % 64 == 0 && kch / 64 <= 2) {
+    L = 64;
+    cpl = kch / 64;
+  } else {
+    return false;
+  }
+  if ((a.topk + 64 / L - 1) / (64 / L) > kDW) return false;
+  hipError_t e2;
+  if (cpl == 1)
+    e2 = launch_dn_t1r<FMT, 64, 1, GROUPED>(a, st);
+  else
+    e2 = launch_dn_t1r<FMT, 64, 2, GROUPED>(a, st);
+  if (e2 == hipErrorNotSupported) return false;
+  *err = e2;
+  return true;
+}
+
 // Stage entry points used by the C ABI: LDS-ring kernels first, then the
 // register-pipelined single-token kernels, then the general decode kernels.
 template <int FMT, int XT, bool GROUPED>
@@ -497,6 +721,7 @@ inline hipError_t stage_gate_up_any(const MoeDecodeArgs& a, hipStream_t st) {
 template <int FMT, bool GROUPED>
 inline hipError_t stage_down_any(const MoeDecodeArgs& a, hipStream_t st) {
   hipError_t err = hipSuccess;
+  if (try_down_t1r<FMT, GROUPED>(a, st, &err)) return err;
   if (try_down_t1l<FMT, GROUPED>(a, st, &err)) return err;
   return stage_down<FMT, GROUPED>(a, st);
 }
