@@ -71,15 +71,25 @@ __host__ __device__ constexpr int ring_slot_bytes() {
 // ---- gate + up ----------------------------------------------------------------
 // L = 64 lanes per row and exactly CB chunks per lane (H = 64 * CB * 32 for
 // int4).  Unit = RU consecutive rows of gate and up of one routed expert.
-template <int FMT, int XT, int CB, int RU, int D, bool GROUPED>
+// PS (packed scales): the unit's RU * 2 scale rows (G floats each, G a
+// multiple of 4, at most 256 floats in all) arrive with one 16-byte DMA per
+// lane instead of one 4-byte DMA per weight block, each lane fetching its own
+// chunk's scale.
+template <int RU, int M, int CB, bool PS>
+__host__ __device__ constexpr int gu_slot_bytes() {
+  return RU * M * CB * 1024 + (PS ? 1024 : RU * M * CB * 256);
+}
+
+template <int FMT, int XT, int CB, int RU, int D, bool GROUPED, bool PS>
 __global__ __launch_bounds__(kThreads) void moe_gate_up_t1l_kernel(MoeDecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int s_e[kTopkMax];
   constexpr bool SPLIT = (FMT == kFmtInt4 && XT == kF32);
   constexpr int M = 2;
-  constexpr int NW = RU * M * CB;  // 1 KiB weight blocks per unit
-  constexpr int U = 2 * NW;        // VMEM operations per unit
-  constexpr int SLOT = ring_slot_bytes<RU, M, CB>();
+  constexpr int NW = RU * M * CB;         // 1 KiB weight blocks per unit
+  constexpr int U = NW + (PS ? 1 : NW);   // VMEM operations per unit
+  constexpr int SLOT = gu_slot_bytes<RU, M, CB, PS>();
+  static_assert(!PS || GROUPED, "packed scales need grouped scales");
   const ExpertArgs& ex = a.ex;
   const int k = a.topk;
   if ((int)threadIdx.x < k) {
@@ -115,9 +125,20 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1l_kernel(MoeDecodeArgs
           const int c = lane + 64 * cb;
           const int blk = (j * M + m) * CB + cb;
           dma16(qrow + (int64_t)c * 16, sd + blk * 1024);
-          dma4(srow + (GROUPED ? (c >> ex.gshift) : 0), sd + NW * 1024 + blk * 256);
+          if constexpr (!PS) dma4(srow + (GROUPED ? (c >> ex.gshift) : 0), sd + NW * 1024 + blk * 256);
         }
       }
+    }
+    if constexpr (PS) {
+      // floats 4f .. 4f+3 of the unit's scale rows [j][m][G]; lanes past the
+      // last piece reload it (no extra traffic)
+      const int G = ex.G_h;
+      const int f = 4 * min(lane, RU * M * G / 4 - 1);
+      const int rm = f / G, g = f - rm * G;
+      const int j = rm / M, m = rm - j * M;
+      const int r = min(row0 + j, ex.I - 1);
+      const float* srow = (m == 0 ? ex.gs : ex.us) + ((int64_t)e * ex.I + r) * G + g;
+      dma16(srow, sd + NW * 1024);
     }
   };
   int head = next_valid(uniform(blockIdx.x * kWaves + wave));
@@ -158,7 +179,9 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1l_kernel(MoeDecodeArgs
         for (int m = 0; m < M; ++m) {
           const int blk = (j * M + m) * CB + cb;
           const u32x4 w = *reinterpret_cast<const u32x4*>(sd + blk * 1024 + lane * 16);
-          const float s = *reinterpret_cast<const float*>(sd + NW * 1024 + blk * 256 + lane * 4);
+          const float s = PS ? *reinterpret_cast<const float*>(sd + NW * 1024 + ((j * M + m) * ex.G_h +
+                                                                                   (c >> ex.gshift)) * 4)
+                             : *reinterpret_cast<const float*>(sd + NW * 1024 + blk * 256 + lane * 4);
           float t;
           if constexpr (FMT == kFmtInt4) {
             t = xo;
@@ -562,10 +585,17 @@ constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 template <int CB>
 constexpr int gu_ru() { return CB >= 3 ? 1 : (CB == 2 ? 1 : 2); }
 
-template <int FMT, int XT, int CB, bool GROUPED>
+template <int FMT, int XT, int CB, bool GROUPED, bool PS = false>
 inline size_t gu_lds_bytes() {
   return align_lds(stage_rows_bytes<FMT, FMT == kFmtInt4 && XT == kF32>(1, 64 * CB)) +
-         (size_t)kWaves * QM_LDS_GU_D * ring_slot_bytes<gu_ru<CB>(), 2, CB>();
+         (size_t)kWaves * QM_LDS_GU_D * gu_slot_bytes<gu_ru<CB>(), 2, CB, PS>();
+}
+
+// packed scales: grouped, G a multiple of 4 with all of a unit's scale rows in
+// 1 KiB, and 16-byte aligned scale rows
+inline bool gu_packed_scales(const MoeDecodeArgs& a, int RU) {
+  const int G = a.ex.G_h;
+  return G % 4 == 0 && RU * 2 * G <= 256 && ((uintptr_t)a.ex.gs & 15) == 0 && ((uintptr_t)a.ex.us & 15) == 0;
 }
 
 template <int FMT, int XT, int CB, bool GROUPED>
@@ -575,9 +605,17 @@ inline hipError_t launch_gu_t1l(const MoeDecodeArgs& a, hipStream_t st) {
   int blocks = (a.topk * ntiles + kWaves - 1) / kWaves;
   const int cap = a.max_blocks > 0 ? a.max_blocks : QM_LDS_GU_BLOCKS;
   if (blocks > cap) blocks = cap;
+  if constexpr (GROUPED) {
+    if (gu_packed_scales(a, RU)) {
+      const size_t lds = gu_lds_bytes<FMT, XT, CB, GROUPED, true>();
+      hipLaunchKernelGGL((moe_gate_up_t1l_kernel<FMT, XT, CB, RU, QM_LDS_GU_D, GROUPED, true>), dim3(blocks),
+                         dim3(kThreads), lds, st, a);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = gu_lds_bytes<FMT, XT, CB, GROUPED>();
-  hipLaunchKernelGGL((moe_gate_up_t1l_kernel<FMT, XT, CB, RU, QM_LDS_GU_D, GROUPED>), dim3(blocks), dim3(kThreads),
-                     lds, st, a);
+  hipLaunchKernelGGL((moe_gate_up_t1l_kernel<FMT, XT, CB, RU, QM_LDS_GU_D, GROUPED, false>), dim3(blocks),
+                     dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
