@@ -39,6 +39,7 @@ def parse():
                    help="copy: a plain 1 GiB device-to-device copy, the reference kernel for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters")
     p.add_argument("--tokens", type=int, default=1)
+    p.add_argument("--batch", type=int, default=1, help="gemv: activations per weight read (qgemm_small when > 1)")
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
     p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
     p.add_argument("--n", type=int, default=6144)
@@ -276,7 +277,7 @@ def bench_gemv(args):
     from int4_expert_gemv_amd import qmoe, synth
     from oracle import ref
 
-    fmt, n, k, gs = args.fmt, args.n, args.k, (args.gs if args.fmt == 4 else 0)
+    fmt, n, k, gs, B = args.fmt, args.n, args.k, (args.gs if args.fmt == 4 else 0), args.batch
     mb = (n * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else n * (k + 4)
     copies = max(1, -(-(1 << 30) // mb))  # at least 1 GiB of distinct weights in rotation
     g = np.random.default_rng([args.seed, 77])
@@ -284,29 +285,40 @@ def bench_gemv(args):
     mats = []
     for c in range(copies):
         mats.append(qmoe.qmat(fmt, dev(qw), dev(s), n, k, gs))
-    x_h = synth.activations(g, (k,), "bf16")
+    x_h = synth.activations(g, (B, k), "bf16")
     x = dev(x_h)
-    y = torch.empty(n, device="cuda")
+    y = torch.empty((B, n), device="cuda")
+
+    def call(m):
+        if B == 1:
+            qmoe.qgemv(m, x[0], y[0])
+        else:
+            qmoe.qgemm_small(m, x, y)
+
     for i in range(args.warmup):
-        qmoe.qgemv(mats[i % copies], x, y)
+        call(mats[i % copies])
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for j in range(args.steps):
-        qmoe.qgemv(mats[j % copies], x, y)
+        call(mats[j % copies])
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    yr, nr = ref.oracle().gemv(fmt, n, k, gs, qw, s, x_h)
-    err = ref.max_norm_err(y.cpu().numpy(), yr, nr)
-    byts = mb + k * 2 + n * 4
+    o = ref.oracle()
+    err = 0.0
+    yh = y.cpu().numpy()
+    for b in range(B):
+        yr, nr = o.gemv(fmt, n, k, gs, qw, s, x_h[b])
+        err = max(err, ref.max_norm_err(yh[b], yr, nr))
+    byts = mb + B * k * 2 + B * n * 4
     gbs = byts / (ms * 1e-3) / 1e9
+    wname = ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else "int8-row"
     return {"metric": "achieved HBM GB/s for quantized GEMV", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "qgemv %dx%d %s, bf16 x, %d weight copies in rotation" %
-                                   (n, k, ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else "int8-row",
-                                    copies)},
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "%s %dx%d %s, bf16 x, batch %d, %d weight copies in rotation" %
+                                   ("qgemv" if B == 1 else "qgemm_small", n, k, wname, B, copies)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None}
