@@ -137,7 +137,8 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  * vector); larger batches run the expert-grouped prefill kernels (bf16 MFMA,
  * hidden vector and fp32 activations rounded to bf16) when the experts
  * qualify -- int4 with a group size (or, per row, a row length) that is a
- * multiple of 64, at most 128 groups per row, hidden % 512 == 0,
+ * multiple of 64, at most 96 groups per row
+ * (a multiple of 4, with 16-byte aligned scale arrays), hidden % 512 == 0,
  * inter % 256 == 0, n_experts <= 8192 -- and otherwise the decode kernels
  * QM_DECODE_MAX_TOKENS tokens at a time.                                   */
 QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,

@@ -94,8 +94,9 @@ hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArg
 hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
-// (or row length, per-row scales) is a multiple of 64 with at most 128 groups
-// per row, hidden % 512 == 0, inter % 256 == 0 and at most 8192 experts.
+// (or row length, per-row scales) is a multiple of 64 with at most 96 groups
+// per row (grouped: a multiple of 4 groups, 16-byte aligned scale arrays),
+// hidden % 512 == 0, inter % 256 == 0 and at most 8192 experts.
 bool moe_prefill_supported(int fmt, int topk, const ExpertArgs& e);
 size_t moe_prefill_workspace(int T, int topk, const ExpertArgs& e);
 hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void* x, const int32_t* ids,

@@ -62,7 +62,7 @@ constexpr int kBK = 128;        // K per pipeline stage (two 64-K chunks)
 constexpr int kGW = 8;          // waves per GEMM workgroup
 constexpr int kGT = 64 * kGW;   // threads per GEMM workgroup
 constexpr int kStages = QM_PF_STAGES;  // LDS ring depth
-constexpr int kGMax = 128;      // scale groups per row the LDS correction table holds
+constexpr int kGMax = 96;       // scale groups per row the LDS correction table holds
 constexpr int kEMax = 8192;     // experts the bucketing block handles in LDS
 
 struct Tile {
@@ -89,7 +89,7 @@ struct GemmArgs {
   int64_t rb;             // bytes per weight row (K / 2)
   int64_t eq, es;         // per-expert stride of the weights (bytes) and scales (floats)
   int N, K;               // output features and reduction length
-  int G, gs_ch;           // scale groups per row, 64-K chunks per group
+  int G, gs_ch, gs_sh;    // scale groups per row, 64-K chunks per group (a power of two when G > 1) and its log2
   const int* hdr;
   const Tile* tiles;
   const int* sorted;
@@ -268,11 +268,16 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t base) {
 // LDS:
 //   A  BM rows x 256 B      16-byte pieces, piece p of row r at slot p ^ (r & 7)
 //   B  512 weight rows x 64 B, piece p of row rr at slot p ^ ((rr >> 2) & 3)
-//   S  2 chunks x 512 weight rows of fp32 scales
+//   S  (grouped scales) one aligned 16-byte piece per weight row holding the
+//      scales of the stage's two 64-K chunks (groups of 64 or more inputs and
+//      G a multiple of 4 put both in one aligned group of four floats)
 // so that the ds_read_b128 operand reads of 8 consecutive lanes hit distinct
-// banks.  Every thread issues the same U DMA operations per stage, which is
-// what the vmcnt waits count; two stages stay in flight while one is used.
-template <int NM, int NS, int MS>
+// banks.  With one scale per row (ROWSC) a lane keeps its columns' scales in
+// registers and no scales move per stage.  Every thread issues the same U
+// DMA operations per stage, which is what the vmcnt waits count; two stages
+// stay in flight while one is used.  (Scales as 4-byte DMA pieces cost as
+// much stream time as the whole weight tile; 16-byte pieces, almost none.)
+template <int NM, int NS, int MS, bool ROWSC>
 struct GemmShape {
   static constexpr int BM = 32 * MS;
   static constexpr int BN = kGW * NS * 32;
@@ -281,20 +286,21 @@ struct GemmShape {
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * kBK * 2;
   static constexpr int S_OFF = B_OFF + ROWS * kBK / 2;
-  static constexpr int SLOT = S_OFF + 2 * ROWS * 4;
+  static constexpr int SLOT = S_OFF + (ROWSC ? 0 : ROWS * 16);
   static constexpr int PA = BM * 16 / kGT;         // A pieces per thread
   static constexpr int PB = ROWS * 4 / kGT;        // B pieces per thread
-  static constexpr int PS = 2 * ROWS / kGT;        // scale pieces per thread
+  static constexpr int PS = ROWSC ? 0 : ROWS / kGT;  // scale pieces per thread
+  static constexpr int PSA = PS > 0 ? PS : 1;        // array extent
   static constexpr int U = PA + PB + PS;            // DMA operations per thread and stage
   static constexpr int CS = BM + 4;                 // correction table row stride (floats)
 };
 
 // DMA of one pipeline stage (A rows, weight rows, scales) into LDS slot `slot`.
 template <typename S>
-__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wave, int gs_ch,
+__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wave, int gs_sh,
                                             const uint16_t* const (&arow)[S::PA], const int (&apiece)[S::PA],
                                             const uint8_t* const (&brow)[S::PB], const int (&bpiece)[S::PB],
-                                            const float* const (&srow)[S::PS]) {
+                                            const float* const (&srow)[S::PSA]) {
   char* sd = lds + slot * S::SLOT;
   const int k0 = st * kBK;
 #pragma unroll
@@ -306,14 +312,14 @@ __device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wav
     __builtin_amdgcn_global_load_lds(brow[i] + k0 / 2 + 16 * bpiece[i],
                                      QM_LDS_PTR(sd + S::B_OFF + (i * kGW + wave) * 1024), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < S::PS; ++i)  // piece i serves chunk (i * kGT) / ROWS of the stage
-    __builtin_amdgcn_global_load_lds(srow[i] + (st * 2 + (i * kGT) / S::ROWS) / gs_ch,
-                                     QM_LDS_PTR(sd + S::S_OFF + (i * kGT + wave * 64) * 4), 4, 0, 0);
+  for (int i = 0; i < S::PS; ++i)  // the aligned four scales holding the stage's groups
+    __builtin_amdgcn_global_load_lds(srow[i] + (((st * 2) >> gs_sh) & ~3),
+                                     QM_LDS_PTR(sd + S::S_OFF + (i * kGT + wave * 64) * 16), 16, 0, 0);
 }
 
-template <int NM, int NS, int MS>
+template <int NM, int NS, int MS, bool ROWSC>
 __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
-  using S = GemmShape<NM, NS, MS>;
+  using S = GemmShape<NM, NS, MS, ROWSC>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int s_row[S::BM];   // A row index of each tile row
   __shared__ int s_pair[S::BM];  // pair index of each tile row
@@ -354,9 +360,9 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     brow[i] = a.wq[mat] + (int64_t)tl.e * a.eq + (int64_t)(n0 + n) * a.rb;
     bpiece[i] = (P & 3) ^ ((rr >> 2) & 3);
   }
-  const float* srow[S::PS];
+  const float* srow[S::PSA];
 #pragma unroll
-  for (int i = 0; i < S::PS; ++i) {
+  for (int i = 0; i < S::PSA; ++i) {
     const int rr = (i * kGT + tid) % S::ROWS;
     const int mat = rr / S::BN, n = rr % S::BN;
     srow[i] = a.wsc[mat] + (int64_t)tl.e * a.es + (int64_t)(n0 + n) * a.G;
@@ -367,12 +373,12 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   // depends on the expert and the column tile only, never on which M-tile a
   // pair landed in (the bucketing order is not fixed), so every output keeps
   // one summation order from run to run.
-  const int spg = a.G == 1 ? 1 : (a.gs_ch >= 2 ? a.gs_ch / 2 : 1);  // stages per scale group
+  const int spg = a.G == 1 ? 1 : (a.gs_ch >= 2 ? a.gs_ch >> 1 : 1);  // stages per scale group
   const int rk = tl.e * 7 + nti * 3;
   const int rot = a.G == 1 ? rk % nstages : (rk % (nstages / spg)) * spg;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < nstages) issue_stage<S>(lds, rotated(i, rot, nstages), i, wave, a.gs_ch, arow, apiece, brow, bpiece, srow);
+    if (i < nstages) issue_stage<S>(lds, rotated(i, rot, nstages), i, wave, a.gs_sh, arow, apiece, brow, bpiece, srow);
 
   // correction table: corr[g][m] = -136 * (sum of group g of A row m)
   for (int idx = tid; idx < S::BM * a.G; idx += kGT) {
@@ -382,6 +388,12 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
 
   const int h = lane >> 5, c32 = lane & 31;
   const int nsub = MS == 1 ? 1 : (tl.mrows + 31) / 32;  // row subtiles holding valid rows
+  float rsc[NM][NS];  // one scale per row: this lane's columns
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+      rsc[m][ns] = ROWSC ? a.wsc[m][(int64_t)tl.e * a.es + n0 + (wave * NS + ns) * 32 + c32] : 0.f;
   uint32_t base = 0x43004300u;
   asm volatile("" : "+v"(base));  // keep the constant in a VGPR (see b_operand)
   f32x16 acc[NM][NS][MS], tmp[NM][NS][MS], ci[MS];
@@ -402,14 +414,14 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     wait_stages<S::U, kStages>(min(kStages - 2, nstages - 1 - it));
     ring_barrier();  // this stage is in LDS for every wave; the previous one's slot is free
     if (it + kStages - 1 < nstages)
-      issue_stage<S>(lds, rotated(it + kStages - 1, rot, nstages), (it + kStages - 1) % kStages, wave, a.gs_ch, arow, apiece, brow,
+      issue_stage<S>(lds, rotated(it + kStages - 1, rot, nstages), (it + kStages - 1) % kStages, wave, a.gs_sh, arow, apiece, brow,
                      bpiece, srow);
     const char* sd = lds + (it % kStages) * S::SLOT;
     const int st = rotated(it, rot, nstages);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int chunk = st * 2 + c;
-      const int g = chunk / a.gs_ch, cin = chunk - g * a.gs_ch;
+      const int g = chunk >> a.gs_sh, cin = chunk & (a.gs_ch - 1);
       // one scale group per row: it spans the whole (rotated) loop
       const bool first = a.G == 1 ? (it == 0 && c == 0) : cin == 0;
       const bool last = a.G == 1 ? (it == nstages - 1 && c == 1) : cin == a.gs_ch - 1;
@@ -463,7 +475,9 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) {
             const int rr = m * S::BN + (wave * NS + ns) * 32 + c32;
-            const float sc = *reinterpret_cast<const float*>(sd + S::S_OFF + (c * S::ROWS + rr) * 4);
+            const float sc = ROWSC ? rsc[m][ns]
+                                   : *reinterpret_cast<const float*>(sd + S::S_OFF + rr * 16 +
+                                                                     (g - (((st * 2) >> a.gs_sh) & ~3)) * 4);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
               if (ms >= nsub) break;
@@ -583,6 +597,10 @@ bool moe_prefill_supported(int fmt, int topk, const ExpertArgs& e) {
   const int gsh = e.H / e.G_h, gsi = e.I / e.G_i;  // group sizes (== K when per row)
   if (gsh % 64 || gsi % 64) return false;
   if (e.G_h > kGMax || e.G_i > kGMax) return false;
+  // grouped scales move as aligned 16-byte pieces: G a multiple of 4, 16-byte aligned scale arrays
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (e.G_h > 1 && (e.G_h % 4 || !al16(e.gs) || !al16(e.us))) return false;
+  if (e.G_i > 1 && (e.G_i % 4 || !al16(e.ds))) return false;
   if ((e.H / 32) > (1 << 16)) return false;
   return true;
 }
@@ -636,7 +654,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
 
   // 2. gate + up
   {
-    using Sh = GemmShape<2, QM_PF_GU_NS, 1>;
+    using Sh = GemmShape<2, QM_PF_GU_NS, 1, false>;
     static_assert(Sh::BM == kBM, "tile rows");
     GemmArgs<2> g{};
     g.wq[0] = e.gq;
@@ -650,6 +668,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.K = e.H;
     g.G = e.G_h;
     g.gs_ch = e.H / e.G_h / 64;
+    g.gs_sh = e.G_h == 1 ? 30 : __builtin_ctz(g.gs_ch);
     g.hdr = hdr;
     g.tiles = tiles;
     g.sorted = sorted;
@@ -662,7 +681,10 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.h32 = h32;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
     const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_h * Sh::CS * 4;
-    hipLaunchKernelGGL((prefill_gemm_kernel<2, QM_PF_GU_NS, 1>), dim3(blocks), dim3(kGT), lds, st, g);
+    if (e.G_h == 1)
+      hipLaunchKernelGGL((prefill_gemm_kernel<2, QM_PF_GU_NS, 1, true>), dim3(blocks), dim3(kGT), lds, st, g);
+    else
+      hipLaunchKernelGGL((prefill_gemm_kernel<2, QM_PF_GU_NS, 1, false>), dim3(blocks), dim3(kGT), lds, st, g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -682,7 +704,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
 
   // 4. down
   {
-    using Sh = GemmShape<1, QM_PF_DN_NS, 1>;
+    using Sh = GemmShape<1, QM_PF_DN_NS, 1, false>;
     static_assert(Sh::BM == kBM, "tile rows");
     GemmArgs<1> g{};
     g.wq[0] = e.dq;
@@ -694,6 +716,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.K = e.I;
     g.G = e.G_i;
     g.gs_ch = e.I / e.G_i / 64;
+    g.gs_sh = e.G_i == 1 ? 30 : __builtin_ctz(g.gs_ch);
     g.hdr = hdr;
     g.tiles = tiles;
     g.sorted = sorted;
@@ -705,7 +728,10 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.out = out;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
     const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_i * Sh::CS * 4;
-    hipLaunchKernelGGL((prefill_gemm_kernel<1, QM_PF_DN_NS, 1>), dim3(blocks), dim3(kGT), lds, st, g);
+    if (e.G_i == 1)
+      hipLaunchKernelGGL((prefill_gemm_kernel<1, QM_PF_DN_NS, 1, true>), dim3(blocks), dim3(kGT), lds, st, g);
+    else
+      hipLaunchKernelGGL((prefill_gemm_kernel<1, QM_PF_DN_NS, 1, false>), dim3(blocks), dim3(kGT), lds, st, g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
