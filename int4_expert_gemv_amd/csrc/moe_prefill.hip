@@ -16,9 +16,11 @@
 // v_mfma_f32_32x32x16_bf16 lane, in the K order n0 n4 n1 n5 n2 n6 n3 n7; the
 // activations are stored once in that same pair-permuted order.  The offset
 // (128 + 8 = 136 per weight) and the fp32 scale of every K group are applied
-// per group: each group's MFMA chain starts from C = -136 * (sum of the
-// group's activations of that row) and is folded into the accumulator with
-// one FMA by the column's scale.  Activations are bf16 (fp32 input is rounded
+// per group: each group's MFMA chain is folded into the accumulator with one
+// FMA by the column's scale, and the offset term scale[n][g] * (-136 * sum of
+// group g of row m) is a rank-2 update per stage -- one fp32
+// v_mfma_f32_32x32x2_f32 over the (at most two) groups that end in the stage,
+// so no VALU work per element goes to it.  Activations are bf16 (fp32 input is rounded
 // to nearest even) and the hidden vector h = silu(gate x) * up x is rounded to
 // bf16 before the down projection -- the prefill precision the oracle models.
 //
@@ -298,9 +300,9 @@ struct GemmShape {
 // DMA of one pipeline stage (A rows, weight rows, scales) into LDS slot `slot`.
 template <typename S>
 __device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wave, int gs_sh,
-                                            const uint16_t* const (&arow)[S::PA], const int (&apiece)[S::PA],
-                                            const uint8_t* const (&brow)[S::PB], const int (&bpiece)[S::PB],
-                                            const float* const (&srow)[S::PSA]) {
+                                            const uint16_t* const* arow, const int* apiece,
+                                            const uint8_t* const* brow, const int* bpiece,
+                                            const float* const* srow) {
   char* sd = lds + slot * S::SLOT;
   const int k0 = st * kBK;
 #pragma unroll
@@ -317,8 +319,14 @@ __device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wav
                                      QM_LDS_PTR(sd + S::S_OFF + (i * kGT + wave * 64) * 16), 16, 0, 0);
 }
 
-template <int NM, int NS, int MS, bool ROWSC>
+// GM, the scale grouping the loop is compiled for: 0 one scale per row,
+// 1 groups of 64 K (every chunk starts and ends a group), 2 groups of 128 K
+// (chunk 0 of a stage starts one, chunk 1 ends it), 3 groups of 256 K or
+// more (decided at run time).  Where a chunk starts a group at compile time
+// its first MFMA takes the inline constant 0 as C.
+template <int NM, int NS, int MS, int GM>
 __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
+  constexpr bool ROWSC = GM == 0;
   using S = GemmShape<NM, NS, MS, ROWSC>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int s_row[S::BM];   // A row index of each tile row
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
       rsc[m][ns] = ROWSC ? a.wsc[m][(int64_t)tl.e * a.es + n0 + (wave * NS + ns) * 32 + c32] : 0.f;
   uint32_t base = 0x43004300u;
   asm volatile("" : "+v"(base));  // keep the constant in a VGPR (see b_operand)
-  f32x16 acc[NM][NS][MS], tmp[NM][NS][MS], ci[MS];
+  f32x16 acc[NM][NS][MS], tmp[NM][NS][MS];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -406,8 +414,6 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
         acc[m][ns][ms] = f32x16{};
         tmp[m][ns][ms] = f32x16{};
       }
-#pragma unroll
-  for (int ms = 0; ms < MS; ++ms) ci[ms] = f32x16{};
 
   for (int it = 0; it < nstages; ++it) {
     // stages issued after this one so far: min(it + kStages - 2, nstages - 1) - it
@@ -422,21 +428,14 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     for (int c = 0; c < 2; ++c) {
       const int chunk = st * 2 + c;
       const int g = chunk >> a.gs_sh, cin = chunk & (a.gs_ch - 1);
-      // one scale group per row: it spans the whole (rotated) loop
-      const bool first = a.G == 1 ? (it == 0 && c == 0) : cin == 0;
-      const bool last = a.G == 1 ? (it == nstages - 1 && c == 1) : cin == a.gs_ch - 1;
-      if (first) {  // first chunk of a group: its MFMA chain starts from the offset correction
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          if (ms >= nsub) break;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(corr + g * S::CS + ms * 32 + 8 * i + 4 * h);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ci[ms][4 * i + j] = v[j];
-          }
-        }
-      }
+      // With one scale per row the group spans the whole (rotated) loop and
+      // the chain runs on from the zeroed tmp; with run-time groups the fold
+      // clears tmp for the next group.
+      const bool first = GM == 1 ? true : GM == 2 ? c == 0 : false;
+      const bool last = GM == 1   ? true
+                        : GM == 2 ? c == 1
+                        : GM == 0 ? (it == nstages - 1 && c == 1)
+                                  : cin == a.gs_ch - 1;
       u32x4 wv[NM][NS];
 #pragma unroll
       for (int m = 0; m < NM; ++m)
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
           for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns)
-              tmp[m][ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo[m][ns], (first && s == 0) ? ci[ms]
+              tmp[m][ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo[m][ns], (first && s == 0) ? f32x16{}
                                                                                                   : tmp[m][ns][ms],
                                                                        0, 0, 0);
         }
@@ -483,9 +482,37 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
               if (ms >= nsub) break;
 #pragma unroll
               for (int i = 0; i < 16; ++i) acc[m][ns][ms][i] = __builtin_fmaf(sc, tmp[m][ns][ms][i], acc[m][ns][ms][i]);
+              if (GM == 3) tmp[m][ns][ms] = f32x16{};
             }
           }
       }
+    }
+    // Offset correction of the groups that ended in this stage, acc[m][n] +=
+    // sc[n][g] * corr[g][m], as one fp32 MFMA 32x32x2 whose two K slots are
+    // the stage's two chunks (lane half h holds chunk h: its group's
+    // correction if the group ends there, else 0, and that group's scale).
+    const int gfirst = (st * 2) >> a.gs_sh, glast = (st * 2 + 1) >> a.gs_sh;
+    const bool end0 = GM == 1 ? true : GM == 3 ? ((st * 2) & (a.gs_ch - 1)) == a.gs_ch - 1 : false;
+    const bool end1 = GM == 1 || GM == 2 ? true : GM == 0 ? it == nstages - 1 : ((st * 2 + 1) & (a.gs_ch - 1)) == a.gs_ch - 1;
+    if (end0 || end1) {
+      const int gh = h ? glast : gfirst;
+      const bool endh = h ? end1 : end0;
+      float av[MS];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) av[ms] = endh ? corr[gh * S::CS + ms * 32 + c32] : 0.f;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int rr = m * S::BN + (wave * NS + ns) * 32 + c32;
+          const float bv = ROWSC ? rsc[m][ns]
+                                 : *reinterpret_cast<const float*>(sd + S::S_OFF + rr * 16 + (gh - (gfirst & ~3)) * 4);
+#pragma unroll
+          for (int ms = 0; ms < MS; ++ms) {
+            if (ms >= nsub) break;
+            acc[m][ns][ms] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ms], bv, acc[m][ns][ms], 0, 0, 0);
+          }
+        }
     }
   }
 
@@ -518,6 +545,19 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
       }
     }
   }
+}
+
+template <int NM, int NS>
+hipError_t launch_gemm(const GemmArgs<NM>& g, int blocks, size_t lds, hipStream_t st) {
+  if (g.G == 1)
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 0>), dim3(blocks), dim3(kGT), lds, st, g);
+  else if (g.gs_ch == 1)
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 1>), dim3(blocks), dim3(kGT), lds, st, g);
+  else if (g.gs_ch == 2)
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 2>), dim3(blocks), dim3(kGT), lds, st, g);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 3>), dim3(blocks), dim3(kGT), lds, st, g);
+  return hipGetLastError();
 }
 
 // ---- 3. group sums of h ---------------------------------------------------------------
@@ -681,11 +721,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.h32 = h32;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
     const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_h * Sh::CS * 4;
-    if (e.G_h == 1)
-      hipLaunchKernelGGL((prefill_gemm_kernel<2, QM_PF_GU_NS, 1, true>), dim3(blocks), dim3(kGT), lds, st, g);
-    else
-      hipLaunchKernelGGL((prefill_gemm_kernel<2, QM_PF_GU_NS, 1, false>), dim3(blocks), dim3(kGT), lds, st, g);
-    err = hipGetLastError();
+    err = launch_gemm<2, QM_PF_GU_NS>(g, blocks, lds, st);
     if (err != hipSuccess) return err;
   }
 
@@ -728,11 +764,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.out = out;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
     const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_i * Sh::CS * 4;
-    if (e.G_i == 1)
-      hipLaunchKernelGGL((prefill_gemm_kernel<1, QM_PF_DN_NS, 1, true>), dim3(blocks), dim3(kGT), lds, st, g);
-    else
-      hipLaunchKernelGGL((prefill_gemm_kernel<1, QM_PF_DN_NS, 1, false>), dim3(blocks), dim3(kGT), lds, st, g);
-    err = hipGetLastError();
+    err = launch_gemm<1, QM_PF_DN_NS>(g, blocks, lds, st);
     if (err != hipSuccess) return err;
   }
 
