@@ -55,13 +55,7 @@ constexpr int kBK = 128;        // K per pipeline stage (two 64-K chunks)
 #ifndef QM_PF_STAGES
 #define QM_PF_STAGES 3
 #endif
-#ifndef QM_PF_GU_NS
-#define QM_PF_GU_NS 1
-#endif
-#ifndef QM_PF_DN_NS
-#define QM_PF_DN_NS 2
-#endif
-constexpr int kGW = 8;          // waves per GEMM workgroup
+constexpr int kGW = 16;         // waves per GEMM workgroup
 constexpr int kGT = 64 * kGW;   // threads per GEMM workgroup
 constexpr int kStages = QM_PF_STAGES;  // LDS ring depth
 constexpr int kGMax = 96;       // scale groups per row the LDS correction table holds
@@ -264,59 +258,71 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t base) {
   return __builtin_bit_cast(bf16x8, p);
 }
 
-// Block: 8 waves; tile = BM = 32 MS rows (tokens) x BN = 8 NS 32 columns of
-// each of the NM matrices; wave w owns columns [32 (w NS + ns), +32) of every
-// matrix and all MS 32-row subtiles.  Per stage (128 K) the block DMAs into
-// LDS:
-//   A  BM rows x 256 B      16-byte pieces, piece p of row r at slot p ^ (r & 7)
-//   B  512 weight rows x 64 B, piece p of row rr at slot p ^ ((rr >> 2) & 3)
-//   S  (grouped scales) one aligned 16-byte piece per weight row holding the
-//      scales of the stage's two 64-K chunks (groups of 64 or more inputs and
-//      G a multiple of 4 put both in one aligned group of four floats)
+// Block: 16 waves over one M-tile of BM = 32 rows (tokens) and 512 weight
+// rows; wave w owns the 32-column tile of weight rows [32 w, 32 w + 32): for
+// gate+up (NM = 2) waves 0-7 hold gate columns and waves 8-15 the up columns
+// of the same 256 outputs, for down (NM = 1) the 512 outputs.  Four waves per
+// SIMD keep the matrix cores, the VALU work that builds B operands and folds
+// groups, and the LDS reads of different waves overlapping.  Per stage
+// (128 K) the block DMAs into LDS:
+//   A  BM rows x 256 B, piece p of row r at slot p ^ (r & 7)   (waves 0-7, one piece each)
+//   B  512 weight rows x 64 B, piece p of row rr at slot p ^ ((rr >> 2) & 3)   (two per thread)
 // so that the ds_read_b128 operand reads of 8 consecutive lanes hit distinct
-// banks.  With one scale per row (ROWSC) a lane keeps its columns' scales in
-// registers and no scales move per stage.  Every thread issues the same U
-// DMA operations per stage, which is what the vmcnt waits count; two stages
-// stay in flight while one is used.  (Scales as 4-byte DMA pieces cost as
-// much stream time as the whole weight tile; 16-byte pieces, almost none.)
-template <int NM, int NS, int MS, bool ROWSC>
+// banks.  Grouped scales move per window of four groups (2 gs_ch stages): one
+// aligned 16-byte piece per weight row (waves 8-15), DMA'd with the window's
+// first stage into one of two window slots outside the stage ring.  Every
+// scale piece is its own 64-byte line access, so loading each piece once per
+// window rather than once per stage halves that request stream, which costs
+// far more per byte than the weight rows.  With one scale per row (ROWSC) a
+// lane keeps its column's scale in a register and no scales move.  Waves 0-7
+// issue UA DMA operations per stage, waves 8-15 PB plus one on window starts:
+// that is what their vmcnt waits count; two stages stay in flight while one
+// is used.
+template <int NM, bool ROWSC_>
 struct GemmShape {
-  static constexpr int BM = 32 * MS;
-  static constexpr int BN = kGW * NS * 32;
-  static constexpr int ROWS = NM * BN;
-  static_assert(ROWS % kGT == 0 && (BM * 16) % kGT == 0, "whole pieces per thread and stage");
+  static constexpr bool ROWSC = ROWSC_;
+  static constexpr int BM = kBM;
+  static constexpr int ROWS = kGW * 32;
+  static constexpr int BN = ROWS / NM;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * kBK * 2;
-  static constexpr int S_OFF = B_OFF + ROWS * kBK / 2;
-  static constexpr int SLOT = S_OFF + (ROWSC ? 0 : ROWS * 16);
-  static constexpr int PA = BM * 16 / kGT;         // A pieces per thread
-  static constexpr int PB = ROWS * 4 / kGT;        // B pieces per thread
-  static constexpr int PS = ROWSC ? 0 : ROWS / kGT;  // scale pieces per thread
-  static constexpr int PSA = PS > 0 ? PS : 1;        // array extent
-  static constexpr int U = PA + PB + PS;            // DMA operations per thread and stage
-  static constexpr int CS = BM + 4;                 // correction table row stride (floats)
+  static constexpr int SLOT = B_OFF + ROWS * kBK / 2;                  // one ring stage
+  static constexpr int SW = ROWS * 16;                                 // one scale-window slot
+  static constexpr int SW_OFF = kStages * SLOT;                        // two window slots
+  static constexpr int CORR_OFF = SW_OFF + (ROWSC ? 0 : 2 * SW);       // correction table
+  static constexpr int PB = ROWS * 4 / kGT;         // B pieces per thread
+  static constexpr int UA = PB + 1;                 // DMA operations per stage, waves 0-7
+  static constexpr int CS = BM;                     // correction table row stride (floats)
+  static_assert(BM * 16 == kGT / 2 && ROWS == kGT / 2 && (ROWS * 4) % kGT == 0, "piece split");
 };
 
-// DMA of one pipeline stage (A rows, weight rows, scales) into LDS slot `slot`.
+template <int NM, typename T>
+__device__ __forceinline__ T pick(T const (&v)[NM], int m) {
+  return NM == 1 || m == 0 ? v[0] : v[NM - 1];
+}
+
+// DMA of one pipeline stage (A rows, weight rows) into LDS slot `slot`, plus
+// the scale window it starts (`win`) into window slot `wslot`.  `wave` and
+// `win` are wave-uniform (SGPRs), so the choices are scalar branches and each
+// wave issues exactly the operations its vmcnt waits count.
 template <typename S>
-__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wave, int gs_sh,
-                                            const uint16_t* const* arow, const int* apiece,
-                                            const uint8_t* const* brow, const int* bpiece,
-                                            const float* const* srow) {
+__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, bool win, int wslot, int wave, int gs_sh,
+                                            const uint16_t* arow, int apiece, const uint8_t* const* brow,
+                                            const int* bpiece, const float* srow) {
   char* sd = lds + slot * S::SLOT;
   const int k0 = st * kBK;
-#pragma unroll
-  for (int i = 0; i < S::PA; ++i)
-    __builtin_amdgcn_global_load_lds(arow[i] + k0 + 8 * apiece[i],
-                                     QM_LDS_PTR(sd + S::A_OFF + (i * kGW + wave) * 1024), 16, 0, 0);
+  if (wave < kGW / 2) {
+    __builtin_amdgcn_global_load_lds(arow + k0 + 8 * apiece, QM_LDS_PTR(sd + S::A_OFF + wave * 1024), 16, 0, 0);
+  } else if constexpr (!S::ROWSC) {
+    if (win)  // the aligned four scales of the window
+      __builtin_amdgcn_global_load_lds(srow + (((st * 2) >> gs_sh) & ~3),
+                                       QM_LDS_PTR(lds + S::SW_OFF + wslot * S::SW + (wave - kGW / 2) * 1024), 16, 0,
+                                       0);
+  }
 #pragma unroll
   for (int i = 0; i < S::PB; ++i)
     __builtin_amdgcn_global_load_lds(brow[i] + k0 / 2 + 16 * bpiece[i],
                                      QM_LDS_PTR(sd + S::B_OFF + (i * kGW + wave) * 1024), 16, 0, 0);
-#pragma unroll
-  for (int i = 0; i < S::PS; ++i)  // the aligned four scales holding the stage's groups
-    __builtin_amdgcn_global_load_lds(srow[i] + (((st * 2) >> gs_sh) & ~3),
-                                     QM_LDS_PTR(sd + S::S_OFF + (i * kGT + wave * 64) * 16), 16, 0, 0);
 }
 
 // GM, the scale grouping the loop is compiled for: 0 one scale per row,
@@ -324,10 +330,11 @@ __device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wav
 // (chunk 0 of a stage starts one, chunk 1 ends it), 3 groups of 256 K or
 // more (decided at run time).  Where a chunk starts a group at compile time
 // its first MFMA takes the inline constant 0 as C.
-template <int NM, int NS, int MS, int GM>
+template <int NM, int GM>
 __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   constexpr bool ROWSC = GM == 0;
-  using S = GemmShape<NM, NS, MS, ROWSC>;
+  using S = GemmShape<NM, ROWSC>;
+  constexpr int HW = kGW / 2;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int s_row[S::BM];   // A row index of each tile row
   __shared__ int s_pair[S::BM];  // pair index of each tile row
@@ -336,7 +343,8 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   const int mt = L % a.mt_max, nti = L / a.mt_max;
   if (nti >= a.nt || mt >= a.hdr[0]) return;
   const Tile tl = a.tiles[mt];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = nti * S::BN;
   if (tid < S::BM) {
     const int r = tid < tl.mrows ? tid : 0;
@@ -346,17 +354,34 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   }
   __syncthreads();
 
-  float* corr = reinterpret_cast<float*>(lds + kStages * S::SLOT);
+  float* corr = reinterpret_cast<float*>(lds + S::CORR_OFF);
   const int nstages = a.K / kBK;
-  // per-thread DMA sources (rows fixed for the whole K loop)
-  const uint16_t* arow[S::PA];
-  int apiece[S::PA];
+  const int h = lane >> 5, c32 = lane & 31;
+  const int mat = wave / (kGW / NM);  // this wave's matrix
+  const int rw = wave * 32 + c32;     // its weight row within the block
+  // correction table sources, loaded before the first DMA so that waiting
+  // for them leaves the stages in flight: corr[g][m] = -136 * (sum of group g of A row m)
+  constexpr int CT = (kBM * kGMax + kGT - 1) / kGT;
+  float cv[CT];
 #pragma unroll
-  for (int i = 0; i < S::PA; ++i) {
-    const int P = (i * kGW + wave) * 64 + lane;
+  for (int j = 0; j < CT; ++j) {
+    const int idx = tid + j * kGT;
+    cv[j] = idx < S::BM * a.G ? a.asum[(int64_t)s_row[idx / a.G] * a.G + idx % a.G] : 0.f;
+  }
+  // one scale per row: this lane's column
+  const float rsc = ROWSC ? pick(a.wsc, mat)[(int64_t)tl.e * a.es + n0 + (wave % (kGW / NM)) * 32 + c32] : 0.f;
+  // per-thread DMA sources (rows fixed for the whole K loop)
+  const uint16_t* arow = a.a;
+  int apiece = 0;
+  const float* srow = a.wsc[0];
+  if (wave < HW) {
+    const int P = wave * 64 + lane;
     const int r = P >> 4;
-    arow[i] = a.a + (int64_t)s_row[r] * a.K;
-    apiece[i] = (P & 15) ^ (r & 7);
+    arow = a.a + (int64_t)s_row[r] * a.K;
+    apiece = (P & 15) ^ (r & 7);
+  } else {
+    const int rr = (wave - HW) * 64 + lane;
+    srow = pick(a.wsc, rr / S::BN) + (int64_t)tl.e * a.es + (int64_t)(n0 + rr % S::BN) * a.G;
   }
   const uint8_t* brow[S::PB];
   int bpiece[S::PB];
@@ -364,16 +389,8 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   for (int i = 0; i < S::PB; ++i) {
     const int P = (i * kGW + wave) * 64 + lane;
     const int rr = P >> 2;
-    const int mat = rr / S::BN, n = rr % S::BN;
-    brow[i] = a.wq[mat] + (int64_t)tl.e * a.eq + (int64_t)(n0 + n) * a.rb;
+    brow[i] = pick(a.wq, rr / S::BN) + (int64_t)tl.e * a.eq + (int64_t)(n0 + rr % S::BN) * a.rb;
     bpiece[i] = (P & 3) ^ ((rr >> 2) & 3);
-  }
-  const float* srow[S::PSA];
-#pragma unroll
-  for (int i = 0; i < S::PSA; ++i) {
-    const int rr = (i * kGT + tid) % S::ROWS;
-    const int mat = rr / S::BN, n = rr % S::BN;
-    srow[i] = a.wsc[mat] + (int64_t)tl.e * a.es + (int64_t)(n0 + n) * a.G;
   }
   // Blocks walk K from different stages (rotated by whole scale groups):
   // weight rows lie a multiple of 1 KiB apart, so blocks that all stood at the
@@ -381,48 +398,44 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   // depends on the expert and the column tile only, never on which M-tile a
   // pair landed in (the bucketing order is not fixed), so every output keeps
   // one summation order from run to run.
-  const int spg = a.G == 1 ? 1 : (a.gs_ch >= 2 ? a.gs_ch >> 1 : 1);  // stages per scale group
+  // Rotation by whole scale windows keeps window starts at loop positions
+  // that are multiples of the window length, so loop position it uses
+  // window slot (it / window) & 1.
+  const int wsh = ROWSC ? 0 : a.gs_sh + 1;  // log2 of the stages per scale window
   const int rk = tl.e * 7 + nti * 3;
-  const int rot = a.G == 1 ? rk % nstages : (rk % (nstages / spg)) * spg;
+  const int rot = ROWSC ? rk % nstages : (rk % (nstages >> wsh)) << wsh;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < nstages) issue_stage<S>(lds, rotated(i, rot, nstages), i, wave, a.gs_sh, arow, apiece, brow, bpiece, srow);
-
-  // correction table: corr[g][m] = -136 * (sum of group g of A row m)
-  for (int idx = tid; idx < S::BM * a.G; idx += kGT) {
-    const int m = idx / a.G, g = idx - m * a.G;
-    corr[g * S::CS + m] = -136.f * a.asum[(int64_t)s_row[m] * a.G + g];
+    if (i < nstages)
+      issue_stage<S>(lds, rotated(i, rot, nstages), i, (i & ((1 << wsh) - 1)) == 0, (i >> wsh) & 1, wave, a.gs_sh, arow,
+                     apiece, brow, bpiece, srow);
+#pragma unroll
+  for (int j = 0; j < CT; ++j) {
+    const int idx = tid + j * kGT;
+    if (idx < S::BM * a.G) corr[(idx % a.G) * S::CS + idx / a.G] = -136.f * cv[j];
   }
 
-  const int h = lane >> 5, c32 = lane & 31;
-  const int nsub = MS == 1 ? 1 : (tl.mrows + 31) / 32;  // row subtiles holding valid rows
-  float rsc[NM][NS];  // one scale per row: this lane's columns
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-      rsc[m][ns] = ROWSC ? a.wsc[m][(int64_t)tl.e * a.es + n0 + (wave * NS + ns) * 32 + c32] : 0.f;
   uint32_t base = 0x43004300u;
   asm volatile("" : "+v"(base));  // keep the constant in a VGPR (see b_operand)
-  f32x16 acc[NM][NS][MS], tmp[NM][NS][MS];
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        acc[m][ns][ms] = f32x16{};
-        tmp[m][ns][ms] = f32x16{};
-      }
-
+  f32x16 acc = {}, tmp = {};
   for (int it = 0; it < nstages; ++it) {
     // stages issued after this one so far: min(it + kStages - 2, nstages - 1) - it
-    wait_stages<S::U, kStages>(min(kStages - 2, nstages - 1 - it));
+    static_assert(kStages == 3, "the waits below count one stage in flight");
+    const int ahead = min(kStages - 2, nstages - 1 - it);
+    if (wave < HW)
+      wait_stages<S::UA, kStages>(ahead);
+    else if (!ROWSC && ahead > 0 && ((it + 1) & ((1 << wsh) - 1)) == 0)
+      wait_stages<S::PB + 1, kStages>(ahead);  // the stage in flight carries a scale window
+    else
+      wait_stages<S::PB, kStages>(ahead);
     ring_barrier();  // this stage is in LDS for every wave; the previous one's slot is free
-    if (it + kStages - 1 < nstages)
-      issue_stage<S>(lds, rotated(it + kStages - 1, rot, nstages), (it + kStages - 1) % kStages, wave, a.gs_sh, arow, apiece, brow,
-                     bpiece, srow);
+    if (it + kStages - 1 < nstages) {
+      const int j = it + kStages - 1;
+      issue_stage<S>(lds, rotated(j, rot, nstages), j % kStages, (j & ((1 << wsh) - 1)) == 0, (j >> wsh) & 1, wave,
+                     a.gs_sh, arow, apiece, brow, bpiece, srow);
+    }
     const char* sd = lds + (it % kStages) * S::SLOT;
+    const char* sw = lds + S::SW_OFF + ((it >> wsh) & 1) * S::SW;  // this stage's scale window
     const int st = rotated(it, rot, nstages);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -436,55 +449,20 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
                         : GM == 2 ? c == 1
                         : GM == 0 ? (it == nstages - 1 && c == 1)
                                   : cin == a.gs_ch - 1;
-      u32x4 wv[NM][NS];
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int rr = m * S::BN + (wave * NS + ns) * 32 + c32;
-          const int p = 2 * c + h;
-          wv[m][ns] = *reinterpret_cast<const u32x4*>(sd + S::B_OFF + rr * 64 + 16 * (p ^ ((rr >> 2) & 3)));
-        }
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(sd + S::B_OFF + rw * 64 + 16 * ((2 * c + h) ^ ((rw >> 2) & 3)));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8 bo[NM][NS];
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns) bo[m][ns] = b_operand(wv[m][ns][s], base);
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          if (ms >= nsub) break;
-          const int r = ms * 32 + c32;
-          const int p = 8 * c + 4 * h + s;
-          const bf16x8 ao = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + r * 256 + 16 * (p ^ (r & 7))));
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
-              tmp[m][ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo[m][ns], (first && s == 0) ? f32x16{}
-                                                                                                  : tmp[m][ns][ms],
-                                                                       0, 0, 0);
-        }
+        const bf16x8 bo = b_operand(wv[s], base);
+        const int p = 8 * c + 4 * h + s;
+        const bf16x8 ao =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + c32 * 256 + 16 * (p ^ (c32 & 7))));
+        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo, (first && s == 0) ? f32x16{} : tmp, 0, 0, 0);
       }
       if (last) {  // last chunk of the group: fold with the column's scale
+        const float sc = ROWSC ? rsc : *reinterpret_cast<const float*>(sw + rw * 16 + (g & 3) * 4);
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns) {
-            const int rr = m * S::BN + (wave * NS + ns) * 32 + c32;
-            const float sc = ROWSC ? rsc[m][ns]
-                                   : *reinterpret_cast<const float*>(sd + S::S_OFF + rr * 16 +
-                                                                     (g - (((st * 2) >> a.gs_sh) & ~3)) * 4);
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-              if (ms >= nsub) break;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) acc[m][ns][ms][i] = __builtin_fmaf(sc, tmp[m][ns][ms][i], acc[m][ns][ms][i]);
-              if (GM == 3) tmp[m][ns][ms] = f32x16{};
-            }
-          }
+        for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(sc, tmp[i], acc[i]);
+        if (GM == 3) tmp = f32x16{};
       }
     }
     // Offset correction of the groups that ended in this stage, acc[m][n] +=
@@ -496,67 +474,58 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     const bool end1 = GM == 1 || GM == 2 ? true : GM == 0 ? it == nstages - 1 : ((st * 2 + 1) & (a.gs_ch - 1)) == a.gs_ch - 1;
     if (end0 || end1) {
       const int gh = h ? glast : gfirst;
-      const bool endh = h ? end1 : end0;
-      float av[MS];
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms) av[ms] = endh ? corr[gh * S::CS + ms * 32 + c32] : 0.f;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int rr = m * S::BN + (wave * NS + ns) * 32 + c32;
-          const float bv = ROWSC ? rsc[m][ns]
-                                 : *reinterpret_cast<const float*>(sd + S::S_OFF + rr * 16 + (gh - (gfirst & ~3)) * 4);
-#pragma unroll
-          for (int ms = 0; ms < MS; ++ms) {
-            if (ms >= nsub) break;
-            acc[m][ns][ms] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[ms], bv, acc[m][ns][ms], 0, 0, 0);
-          }
-        }
+      const float av = (h ? end1 : end0) ? corr[gh * S::CS + c32] : 0.f;
+      const float bv = ROWSC ? rsc : *reinterpret_cast<const float*>(sw + rw * 16 + (gh & 3) * 4);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
   }
 
   // epilogue; C layout: element 4i + j of a lane is row 8i + 4h + j, column lane & 31
+  if constexpr (NM == 2) {
+    // the up waves hand their tiles to the gate waves of the same columns
+    __syncthreads();  // every wave is done with the ring (no DMA outstanding after the last stage)
+    float* xch = reinterpret_cast<float*>(lds);
+    if (wave >= HW) {
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns) {
-    const int col = n0 + (wave * NS + ns) * 32 + c32;
+      for (int i = 0; i < 16; ++i) xch[((wave - HW) * 16 + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave < HW) {
+      const int col = n0 + wave * 32 + c32;
+      const int pc = (col & ~7) | ((col & 7) < 4 ? 2 * (col & 7) : 2 * (col & 7) - 7);
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      if (ms >= nsub) break;
-      if constexpr (NM == 2) {
-        const int pc = (col & ~7) | ((col & 7) < 4 ? 2 * (col & 7) : 2 * (col & 7) - 7);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = ms * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const uint32_t hb = f32_to_bf16_bits(silu(acc[0][ns][ms][i]) * acc[1][ns][ms][i]);
-          const float sum = group_sum<32>(bf16_bits_to_f32(hb));
-          if (row < tl.mrows) {
-            const int64_t pos = tl.pos0 + row;
-            a.h[pos * a.N + pc] = (uint16_t)hb;
-            if (c32 == 0) a.h32[pos * (a.N / 32) + col / 32] = sum;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = ms * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (row < tl.mrows) a.out[(int64_t)s_pair[row] * a.N + col] = acc[0][ns][ms][i];
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+        const float up = xch[(wave * 16 + i) * 64 + lane];
+        const uint32_t hb = f32_to_bf16_bits(silu(acc[i]) * up);
+        const float sum = group_sum<32>(bf16_bits_to_f32(hb));
+        if (row < tl.mrows) {
+          const int64_t pos = tl.pos0 + row;
+          a.h[pos * a.N + pc] = (uint16_t)hb;
+          if (c32 == 0) a.h32[pos * (a.N / 32) + col / 32] = sum;
         }
       }
+    }
+  } else {
+    const int col = n0 + wave * 32 + c32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+      if (row < tl.mrows) a.out[(int64_t)s_pair[row] * a.N + col] = acc[i];
     }
   }
 }
 
-template <int NM, int NS>
+template <int NM>
 hipError_t launch_gemm(const GemmArgs<NM>& g, int blocks, size_t lds, hipStream_t st) {
   if (g.G == 1)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 0>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 0>), dim3(blocks), dim3(kGT), lds, st, g);
   else if (g.gs_ch == 1)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 1>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 1>), dim3(blocks), dim3(kGT), lds, st, g);
   else if (g.gs_ch == 2)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 2>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 2>), dim3(blocks), dim3(kGT), lds, st, g);
   else
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, NS, 1, 3>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 3>), dim3(blocks), dim3(kGT), lds, st, g);
   return hipGetLastError();
 }
 
@@ -694,7 +663,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
 
   // 2. gate + up
   {
-    using Sh = GemmShape<2, QM_PF_GU_NS, 1, false>;
+    using Sh = GemmShape<2, false>;
     static_assert(Sh::BM == kBM, "tile rows");
     GemmArgs<2> g{};
     g.wq[0] = e.gq;
@@ -720,8 +689,8 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.h = hs;
     g.h32 = h32;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
-    const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_h * Sh::CS * 4;
-    err = launch_gemm<2, QM_PF_GU_NS>(g, blocks, lds, st);
+    const size_t lds = (size_t)Sh::CORR_OFF + (size_t)e.G_h * Sh::CS * 4;
+    err = launch_gemm<2>(g, blocks, lds, st);
     if (err != hipSuccess) return err;
   }
 
@@ -740,7 +709,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
 
   // 4. down
   {
-    using Sh = GemmShape<1, QM_PF_DN_NS, 1, false>;
+    using Sh = GemmShape<1, false>;
     static_assert(Sh::BM == kBM, "tile rows");
     GemmArgs<1> g{};
     g.wq[0] = e.dq;
@@ -763,8 +732,8 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.nt = e.H / Sh::BN;
     g.out = out;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
-    const size_t lds = (size_t)kStages * Sh::SLOT + (size_t)e.G_i * Sh::CS * 4;
-    err = launch_gemm<1, QM_PF_DN_NS>(g, blocks, lds, st);
+    const size_t lds = (size_t)Sh::CORR_OFF + (size_t)e.G_i * Sh::CS * 4;
+    err = launch_gemm<1>(g, blocks, lds, st);
     if (err != hipSuccess) return err;
   }
 
