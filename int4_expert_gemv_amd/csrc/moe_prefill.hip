@@ -265,9 +265,9 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t base) {
 // SIMD keep the matrix cores, the VALU work that builds B operands and folds
 // groups, and the LDS reads of different waves overlapping.  Per stage
 // (128 K) the block DMAs into LDS:
-//   A  BM rows x 256 B, piece p of row r at slot p ^ (r & 7)   (waves 0-7, one piece each)
+//   A  BM rows x 256 B, piece p of row r at slot p ^ (r & 15)  (waves 0-7, one piece each)
 //   B  512 weight rows x 64 B, piece p of row rr at slot p ^ ((rr >> 2) & 3)   (two per thread)
-// so that the ds_read_b128 operand reads of 8 consecutive lanes hit distinct
+// so that the ds_read_b128 operand reads of 16 consecutive lanes hit distinct
 // banks.  Grouped scales move per window of four groups (2 gs_ch stages): one
 // aligned 16-byte piece per weight row (waves 8-15), DMA'd with the window's
 // first stage into one of two window slots outside the stage ring.  Every
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     const int P = wave * 64 + lane;
     const int r = P >> 4;
     arow = a.a + (int64_t)s_row[r] * a.K;
-    apiece = (P & 15) ^ (r & 7);
+    apiece = (P & 15) ^ (r & 15);
   } else {
     const int rr = (wave - HW) * 64 + lane;
     srow = pick(a.wsc, rr / S::BN) + (int64_t)tl.e * a.es + (int64_t)(n0 + rr % S::BN) * a.G;
@@ -429,11 +429,6 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     else
       wait_stages<S::PB, kStages>(ahead);
     ring_barrier();  // this stage is in LDS for every wave; the previous one's slot is free
-    if (it + kStages - 1 < nstages) {
-      const int j = it + kStages - 1;
-      issue_stage<S>(lds, rotated(j, rot, nstages), j % kStages, (j & ((1 << wsh) - 1)) == 0, (j >> wsh) & 1, wave,
-                     a.gs_sh, arow, apiece, brow, bpiece, srow);
-    }
     const char* sd = lds + (it % kStages) * S::SLOT;
     const char* sw = lds + S::SW_OFF + ((it >> wsh) & 1) * S::SW;  // this stage's scale window
     const int st = rotated(it, rot, nstages);
@@ -455,7 +450,7 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
         const bf16x8 bo = b_operand(wv[s], base);
         const int p = 8 * c + 4 * h + s;
         const bf16x8 ao =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + c32 * 256 + 16 * (p ^ (c32 & 7))));
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + c32 * 256 + 16 * (p ^ (c32 & 15))));
         tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo, (first && s == 0) ? f32x16{} : tmp, 0, 0, 0);
       }
       if (last) {  // last chunk of the group: fold with the column's scale
@@ -477,6 +472,15 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
       const float av = (h ? end1 : end0) ? corr[gh * S::CS + c32] : 0.f;
       const float bv = ROWSC ? rsc : *reinterpret_cast<const float*>(sw + rw * 16 + (gh & 3) * 4);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    // The next DMA goes out after this stage's compute: when the memory
+    // pipeline's queues are full an issuing wave stalls in order, and issued
+    // before the compute that stall would hold the MFMA and VALU work too.
+    // The slot it fills was released at this iteration's barrier.
+    if (it + kStages - 1 < nstages) {
+      const int j = it + kStages - 1;
+      issue_stage<S>(lds, rotated(j, rot, nstages), j % kStages, (j & ((1 << wsh) - 1)) == 0, (j >> wsh) & 1, wave,
+                     a.gs_sh, arow, apiece, brow, bpiece, srow);
     }
   }
 
