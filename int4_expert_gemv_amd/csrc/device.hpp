@@ -100,6 +100,28 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// The token's valid routed pairs in slot order -- expert id, slot, routing
+// weight -- compacted by wave 0 with the slots read in parallel (one load
+// latency rather than one per slot); the caller's __syncthreads() publishes
+// them.  topk <= kTopkMax <= 64.
+__device__ __forceinline__ void routed_pairs(const int32_t* ids, const float* w, int topk, int E, int* s_e,
+                                             int* s_p, float* s_w, int* s_n) {
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    const int id = j < topk ? ids[j] : -1;
+    const float wj = j < topk ? w[j] : 0.f;
+    const bool ok = id >= 0 && id < E;
+    const unsigned long long m = __ballot(ok);
+    const int n = __popcll(m & ((1ull << j) - 1));
+    if (ok) {
+      s_e[n] = id;
+      s_p[n] = j;
+      s_w[n] = wj;
+    }
+    if (j == 0) *s_n = __popcll(m);
+  }
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Sum over aligned groups of L lanes; every lane of a group ends with the sum.

@@ -127,19 +127,7 @@ __global__ __launch_bounds__(kThreads) QM_T1_OCC void moe_down_t1_kernel(MoeDeco
   constexpr int M = 1;
   constexpr int RU = ru_for(M, CB) > 4 ? 4 : ru_for(M, CB);
   const ExpertArgs& ex = a.ex;
-  if (threadIdx.x == 0) {  // valid pairs of the token, in slot order
-    int n = 0;
-    for (int j = 0; j < a.topk; ++j) {
-      const int id = a.ids[j];
-      if (id >= 0 && id < ex.E) {
-        s_e[n] = id;
-        s_p[n] = j;
-        s_w[n] = a.w[j];
-        ++n;
-      }
-    }
-    s_n = n;
-  }
+  routed_pairs(a.ids, a.w, a.topk, ex.E, s_e, s_p, s_w, &s_n);  // valid pairs of the token, in slot order
   __syncthreads();
   const int np = s_n;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;

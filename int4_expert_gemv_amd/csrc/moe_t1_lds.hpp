@@ -204,19 +204,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_t1l_kernel(MoeDecodeArgs a)
   constexpr int U = 2 * NW;
   constexpr int SLOT = ring_slot_bytes<RU, M, CB>();
   const ExpertArgs& ex = a.ex;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int j = 0; j < a.topk; ++j) {
-      const int id = a.ids[j];
-      if (id >= 0 && id < ex.E) {
-        s_e[n] = id;
-        s_p[n] = j;
-        s_w[n] = a.w[j];
-        ++n;
-      }
-    }
-    s_n = n;
-  }
+  routed_pairs(a.ids, a.w, a.topk, ex.E, s_e, s_p, s_w, &s_n);  // valid pairs of the token, in slot order
   __syncthreads();
   const int np = s_n;
   if (np == 0) {
@@ -384,19 +372,7 @@ __global__ __launch_bounds__(kDT) void moe_down_t1r_kernel(MoeDecodeArgs a) {
   constexpr int SLOT = ring_slot_bytes<1, 1, CPL>();
   constexpr int PER = Fmt<FMT>::kPerChunk;
   const ExpertArgs& ex = a.ex;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int j = 0; j < a.topk; ++j) {
-      const int id = a.ids[j];
-      if (id >= 0 && id < ex.E) {
-        s_e[n] = id;
-        s_p[n] = j;
-        s_w[n] = a.w[j];
-        ++n;
-      }
-    }
-    s_n = n;
-  }
+  routed_pairs(a.ids, a.w, a.topk, ex.E, s_e, s_p, s_w, &s_n);  // valid pairs of the token, in slot order
   __syncthreads();
   const int np = s_n;
   const int npg = (np + PPW - 1) / PPW;  // pair groups: waves per row slice
