@@ -39,6 +39,9 @@ def parse():
                    help="copy: a plain 1 GiB device-to-device copy, the reference kernel for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters")
     p.add_argument("--tokens", type=int, default=1)
+    p.add_argument("--shared", type=int, default=0,
+                   help="moe configs: fold a shared expert into the routed group as one more slot (weight 1); "
+                        "the value is the number of rotating copies of it (one per layer of a model)")
     p.add_argument("--batch", type=int, default=1, help="gemv: activations per weight read (qgemm_small when > 1)")
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
     p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
@@ -106,15 +109,21 @@ def bench_moe(args, E, H, I):
     from oracle import ref
 
     T, k, gs, fmt = args.tokens, 8, args.gs, 4
+    nsh = max(0, args.shared)
     n_steps = args.warmup + args.steps
-    print("generating %d experts (hidden %d, inter %d, int4 gs=%d)" % (E, H, I, gs), file=sys.stderr, flush=True)
+    print("generating %d experts (hidden %d, inter %d, int4 gs=%d)" % (E + nsh, H, I, gs), file=sys.stderr, flush=True)
     t0 = time.time()
-    ex = synth.expert_set(args.seed, fmt, E, H, I, gs, threads=min(16, os.cpu_count() or 4))
+    ex = synth.expert_set(args.seed, fmt, E + nsh, H, I, gs, threads=min(16, os.cpu_count() or 4))
     d = {key: dev(ex[key]) for key in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}
     torch.cuda.synchronize()
     print("generated+uploaded in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
     e = qmoe.experts(fmt, gs, d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
     ids_h, w_h = routing_schedule(args.seed, n_steps, T, E, k)
+    if nsh:  # the shared expert (copy i % nsh at step i) as an always-on slot with weight 1
+        sh_ids = (E + np.arange(n_steps) % nsh).astype(np.int32)
+        ids_h = np.concatenate([ids_h, np.broadcast_to(sh_ids[:, None, None], (n_steps, T, 1))], axis=2)
+        w_h = np.concatenate([w_h, np.ones((n_steps, T, 1), np.float32)], axis=2)
+        k += 1
     x_h = synth.activations(np.random.default_rng([args.seed, 5]), (n_steps, T, H), "bf16")
     ids_d, w_d, x_d = dev(ids_h), dev(w_h), dev(x_h)
     ws = torch.empty(qmoe.moe_expert_ffn_workspace(e, T, k), dtype=torch.uint8, device="cuda")
@@ -135,6 +144,31 @@ def bench_moe(args, E, H, I):
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
+
+    separate_us = None
+    if nsh:  # the same layer with the shared expert as a second call, added by the caller
+        y1 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        y2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        ids_r, w_r = ids_d[:, :, :k - 1].contiguous(), w_d[:, :, :k - 1].contiguous()
+        ids_s, w_s = ids_d[:, :, k - 1:].contiguous(), w_d[:, :, k - 1:].contiguous()
+
+        def sep(i):
+            qmoe.moe_expert_ffn(e, x_d[i], ids_r[i], w_r[i], y1, ws)
+            qmoe.moe_expert_ffn(e, x_d[i], ids_s[i], w_s[i], y2, ws)
+            torch.add(y1, y2, out=y[i])
+
+        for i in range(args.warmup):
+            sep(i)
+        torch.cuda.synchronize()
+        start.record()
+        for j in range(args.steps):
+            sep(args.warmup + j)
+        end.record()
+        torch.cuda.synchronize()
+        separate_us = start.elapsed_time(end) / args.steps * 1e3
+        for j in range(n_steps):  # restore the folded results for the parity check below
+            step(j)
+        torch.cuda.synchronize()
 
     # dominant kernel: the fused gate+up+SiLU stage launched back to back over
     # the same routing draws (events on the launch stream around the launches)
@@ -182,13 +216,17 @@ def bench_moe(args, E, H, I):
                          "%.2f ms per step" % (done, done - 1, 1e3 * el / max(done, 1))}
 
     gname = "g%d" % gs if gs else "row"
-    tag = "%s_%s_t%d" % (args.config, gname, T)
+    tag = "%s_%s_t%d%s" % (args.config, gname, T, "_shared" if nsh else "")
+    routing = "top-%d" % k
+    if nsh:
+        routing = ("top-%d + 1 shared expert folded in as an always-on slot with weight 1 (%d rotating copies)"
+                   % (k - 1, nsh))
     return {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_layer": round(ms_step * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, top-%d, %d token(s), "
-                               "int4-%s weights, bf16 x" % (H, E, I, k, T, gname),
+        "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, %s, %d token(s), "
+                               "int4-%s weights, bf16 x" % (H, E, I, routing, T, gname),
                    "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": "int4-" + gname,
                    "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -198,6 +236,8 @@ def bench_moe(args, E, H, I):
                      "bytes_per_launch": int(gu_bytes)},
         "parity": {"max_norm_err": err, "tol": 2e-4, "stage_entry_points_identical": same},
         "cpu_baseline": cpu,
+        **({"shared_expert": {"separate_call_us_per_layer": round(separate_us, 3),
+                              "folded_us_per_layer": round(ms_step * 1e3, 3)}} if nsh else {}),
     }
 
 

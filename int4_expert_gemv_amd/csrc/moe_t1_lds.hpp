@@ -629,13 +629,14 @@ inline bool try_down_t1l(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err
 
 template <int FMT, int L, int CPL, bool GROUPED>
 inline hipError_t launch_dn_t1r(const MoeDecodeArgs& a, hipStream_t st) {
-  constexpr int D = CPL == 1 ? QM_DOWN_REG_D : (QM_DOWN_REG_D + 1) / 2;
+  // two pairs per wave (L = 32): the full ring depth, one block per CU
+  constexpr int D = (CPL == 1 || L == 32) ? QM_DOWN_REG_D : (QM_DOWN_REG_D + 1) / 2;
   constexpr int PPW = 64 / L;
   const int npg = (a.topk + PPW - 1) / PPW;
   int npg2 = 1;
   while (npg2 < npg) npg2 <<= 1;
   const int S = kDW / npg2;
-  int blocks = a.max_blocks > 0 ? a.max_blocks : QM_DOWN_REG_BLOCKS;
+  int blocks = a.max_blocks > 0 ? a.max_blocks : (L == 32 ? QM_DOWN_REG_BLOCKS / 2 : QM_DOWN_REG_BLOCKS);
   if (blocks > (a.ex.H + S - 1) / S) blocks = (a.ex.H + S - 1) / S;
   const int R = (a.ex.H + blocks - 1) / blocks;
   const size_t lds = (size_t)kDW * D * ring_slot_bytes<1, 1, CPL>() + (size_t)R * kDW * 64 * 4;
@@ -645,7 +646,9 @@ inline hipError_t launch_dn_t1r(const MoeDecodeArgs& a, hipStream_t st) {
 }
 
 // Register-h down kernel: T = 1, each row's chunks over 64 lanes with one or
-// two chunks per lane (one wave per routed pair), at most kDW pairs.
+// two chunks per lane (one wave per routed pair, at most kDW pairs), or, for
+// kDW < top_k <= 2 kDW (a shared expert folded in as a ninth slot), over 32
+// lanes with two pairs per wave.
 template <int FMT, bool GROUPED>
 inline bool try_down_t1r(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err) {
   if (!QM_DOWN_REG || a.T != 1 || a.topk > kTopkMax) return false;
@@ -654,15 +657,20 @@ inline bool try_down_t1r(const MoeDecodeArgs& a, hipStream_t st, hipError_t* err
   // Short rows (fewer than 64 chunks) finish faster in the shared-LDS kernel,
   // whose startup is shorter; the register-h kernel takes rows of 64 or 128
   // chunks (inter 2048 / 4096 for int4).
-  if (kch % 64 == 0 && kch / 64 <= 2) {
+  if (kch % 64 == 0 && kch / 64 <= 2 && a.topk <= kDW) {
     L = 64;
     cpl = kch / 64;
+  } else if (kch == 64 && (a.topk + 1) / 2 <= kDW) {
+    L = 32;
+    cpl = 2;
   } else {
     return false;
   }
   if ((a.topk + 64 / L - 1) / (64 / L) > kDW) return false;
   hipError_t e2;
-  if (cpl == 1)
+  if (L == 32)
+    e2 = launch_dn_t1r<FMT, 32, 2, GROUPED>(a, st);
+  else if (cpl == 1)
     e2 = launch_dn_t1r<FMT, 64, 1, GROUPED>(a, st);
   else
     e2 = launch_dn_t1r<FMT, 64, 2, GROUPED>(a, st);
