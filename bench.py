@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
     p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
     p.add_argument("--n", type=int, default=6144)
+    p.add_argument("--pair", type=int, default=0,
+                   help="gemv: rows of a second matrix of the same x and format, run with qgemv_pair "
+                        "(one launch for both projections); also times the two as separate qgemv calls")
     p.add_argument("--k", type=int, default=6144)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
@@ -318,50 +321,71 @@ def bench_gemv(args):
     from oracle import ref
 
     fmt, n, k, gs, B = args.fmt, args.n, args.k, (args.gs if args.fmt == 4 else 0), args.batch
-    mb = (n * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else n * (k + 4)
+    n2 = args.pair if B == 1 else 0
+    row_b = lambda rows: (rows * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else rows * (k + 4)
+    mb = row_b(n) + row_b(n2)
     copies = max(1, -(-(1 << 30) // mb))  # at least 1 GiB of distinct weights in rotation
     g = np.random.default_rng([args.seed, 77])
     qw, s = synth.quant_matrix(g, fmt, n, k, gs)
     mats = []
     for c in range(copies):
         mats.append(qmoe.qmat(fmt, dev(qw), dev(s), n, k, gs))
+    if n2:
+        qw2, s2 = synth.quant_matrix(np.random.default_rng([args.seed, 78]), fmt, n2, k, gs)
+        mats2 = [qmoe.qmat(fmt, dev(qw2), dev(s2), n2, k, gs) for c in range(copies)]
+        y2 = torch.empty((n2,), device="cuda")
     x_h = synth.activations(g, (B, k), "bf16")
     x = dev(x_h)
     y = torch.empty((B, n), device="cuda")
 
-    def call(m):
-        if B == 1:
-            qmoe.qgemv(m, x[0], y[0])
+    def call(i):
+        if n2:
+            qmoe.qgemv_pair(mats[i], mats2[i], x[0], y[0], y2)
+        elif B == 1:
+            qmoe.qgemv(mats[i], x[0], y[0])
         else:
-            qmoe.qgemm_small(m, x, y)
+            qmoe.qgemm_small(mats[i], x, y)
 
-    for i in range(args.warmup):
-        call(mats[i % copies])
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for j in range(args.steps):
-        call(mats[j % copies])
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    def call_separate(i):
+        qmoe.qgemv(mats[i], x[0], y[0])
+        qmoe.qgemv(mats2[i], x[0], y2)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for j in range(args.steps):
+            fn(j % copies)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    sep_ms = timed(call_separate) if n2 else None
+    ms = timed(call)
     o = ref.oracle()
     err = 0.0
     yh = y.cpu().numpy()
     for b in range(B):
         yr, nr = o.gemv(fmt, n, k, gs, qw, s, x_h[b])
         err = max(err, ref.max_norm_err(yh[b], yr, nr))
-    byts = mb + B * k * 2 + B * n * 4
+    if n2:
+        yr, nr = o.gemv(fmt, n2, k, gs, qw2, s2, x_h[0])
+        err = max(err, ref.max_norm_err(y2.cpu().numpy(), yr, nr))
+    byts = mb + B * k * 2 + B * (n + n2) * 4
     gbs = byts / (ms * 1e-3) / 1e9
     wname = ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else "int8-row"
     return {"metric": "achieved HBM GB/s for quantized GEMV", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 3),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "%s %dx%d %s, bf16 x, batch %d, %d weight copies in rotation" %
-                                   ("qgemv" if B == 1 else "qgemm_small", n, k, wname, B, copies)},
+            "config": {"workload": ("qgemv_pair %dx%d + %dx%d" % (n, k, n2, k) if n2 else
+                                    "%s %dx%d" % ("qgemv" if B == 1 else "qgemm_small", n, k)) +
+                                   " %s, bf16 x, batch %d, %d weight copies in rotation" % (wname, B, copies)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None}
+            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,
+            **({"separate_calls_us": round(sep_ms * 1e3, 3)} if n2 else {})}
 
 
 def bench_copy(args):

@@ -107,6 +107,16 @@ typedef struct {
  * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).       */
 QM_API int qgemv(const qm_qmat *w, const void *x, int32_t x_dtype, float *y, void *stream);
 
+/* Two projections of one x: y1 = W1 x and y2 = W2 x (W1, W2 with the same k).
+ * [V: PR summary, dense tier -- the two attention-input projections of one
+ * x share a submission (the matmul_pair path)]  With the same format and group size and a bf16 x both
+ * run in one launch (x staged once per workgroup, one dispatch instead of
+ * two); otherwise as two launches on the stream.  x: device, k elements.
+ * y1, y2: device, w1->n and w2->n fp32 (overwritten, must not overlap).
+ * Both matrices are validated before anything is enqueued.                  */
+QM_API int qgemv_pair(const qm_qmat *w1, const qm_qmat *w2, const void *x, int32_t x_dtype, float *y1, float *y2,
+                      void *stream);
+
 /* Y[t][r] = sum_c W[r][c] * X[t][c] for t < batch, reading W once for all
  * t.  [V: qmatmul.comp note -- the S-token batch of the same GEMV]
  * x: device [batch][ldx] (ldx >= k, ldx*elemsize a multiple of 16 bytes).

@@ -53,6 +53,10 @@ int rows_per_unit(int L, int NB);
 int seg_chunks(int fmt, int xdt, int NB, int kchunks);
 size_t stage_bytes(int fmt, int xdt, int NB, int segc);
 hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a, int NB, hipStream_t st);
+// Two GEMVs of one x (same fmt, group structure and k) in one launch of the
+// pipelined kernel; hipErrorNotSupported when that kernel does not take them
+// (the caller then launches them one by one).
+hipError_t launch_qgemv_pair(int fmt, int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st);
 hipError_t launch_fill_zero(float* y, int64_t n, int64_t ld, int rows, hipStream_t st);
 
 // per-instantiation launchers (qgemv_*.hip): grouped (_g) or row-scaled (_r)
@@ -65,7 +69,7 @@ QM_DECL_QGEMV(qgemv_launch_i4_f32_r)
 QM_DECL_QGEMV(qgemv_launch_i8_bf16_r)
 QM_DECL_QGEMV(qgemv_launch_i8_f32_r)
 #define QM_DECL_QGEMV2(name) \
-  hipError_t name(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st);
+  hipError_t name(const GemvArgs& a, const GemvArgs& b, int na, int L, int CB, int blocks, size_t lds, hipStream_t st);
 QM_DECL_QGEMV2(qgemv_v2_i4_bf16_g)
 QM_DECL_QGEMV2(qgemv_v2_i4_bf16_r)
 QM_DECL_QGEMV2(qgemv_v2_i8_bf16_r)

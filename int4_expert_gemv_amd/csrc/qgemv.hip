@@ -73,8 +73,9 @@ hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a0, int 
     const size_t lds = stage_bytes(fmt, xdt, 1, kchunks);
     a.segc = kchunks;
     if (fmt == kFmtInt4)
-      return grouped ? qgemv_v2_i4_bf16_g(a, L, CB, blocks, lds, st) : qgemv_v2_i4_bf16_r(a, L, CB, blocks, lds, st);
-    return qgemv_v2_i8_bf16_r(a, L, CB, blocks, lds, st);
+      return grouped ? qgemv_v2_i4_bf16_g(a, a, blocks, L, CB, blocks, lds, st)
+                     : qgemv_v2_i4_bf16_r(a, a, blocks, L, CB, blocks, lds, st);
+    return qgemv_v2_i8_bf16_r(a, a, blocks, L, CB, blocks, lds, st);
   }
   a.segc = seg_chunks(fmt, xdt, NB, kchunks);
   const int tiles = (a.n + rows_per_unit(L, NB) - 1) / rows_per_unit(L, NB);
@@ -90,6 +91,25 @@ hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a0, int 
   }
   return xdt == kBF16 ? qgemv_launch_i8_bf16_r(a, L, NB, blocks, lds, st)
                       : qgemv_launch_i8_f32_r(a, L, NB, blocks, lds, st);
+}
+
+hipError_t launch_qgemv_pair(int fmt, int xdt, bool grouped, const GemvArgs& a0, const GemvArgs& b0, hipStream_t st) {
+  GemvArgs a = a0, b = b0;
+  const int kchunks = a.k / (fmt == kFmtInt4 ? 32 : 16);
+  const int L = lanes_per_row(kchunks);
+  if (xdt != kBF16 || L < 16 || a.k != b.k || stage_bytes(fmt, xdt, 1, kchunks) > (size_t)kLdsBudget)
+    return hipErrorNotSupported;
+  const int CB = v2_cb(kchunks, L);
+  const int RU = 8 / CB >= 8 ? 8 : (8 / CB >= 4 ? 4 : (8 / CB >= 2 ? 2 : 1));
+  const int tile_rows = (64 / L) * RU;
+  const int na = v2_blocks((a.n + tile_rows - 1) / tile_rows, a.max_blocks);
+  const int nb = v2_blocks((b.n + tile_rows - 1) / tile_rows, b.max_blocks);
+  const size_t lds = stage_bytes(fmt, xdt, 1, kchunks);
+  a.segc = b.segc = kchunks;
+  if (fmt == kFmtInt4)
+    return grouped ? qgemv_v2_i4_bf16_g(a, b, na, L, CB, na + nb, lds, st)
+                   : qgemv_v2_i4_bf16_r(a, b, na, L, CB, na + nb, lds, st);
+  return qgemv_v2_i8_bf16_r(a, b, na, L, CB, na + nb, lds, st);
 }
 
 hipError_t launch_fill_zero(float* y, int64_t n, int64_t ld, int rows, hipStream_t st) {

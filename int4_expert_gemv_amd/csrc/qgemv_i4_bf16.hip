@@ -12,12 +12,14 @@ hipError_t qgemv_launch_i4_bf16_r(const GemvArgs& a, int L, int NB, int blocks, 
   return launch_g<kFmtInt4, kBF16, false>(a, L, NB, blocks, lds, st);
 }
 
-hipError_t qgemv_v2_i4_bf16_g(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st) {
-  return launch_v2<kFmtInt4, kBF16, true>(a, L, CB, blocks, lds, st);
+hipError_t qgemv_v2_i4_bf16_g(const GemvArgs& a, const GemvArgs& b, int na, int L, int CB, int blocks, size_t lds,
+                  hipStream_t st) {
+  return launch_v2<kFmtInt4, kBF16, true>(a, b, na, L, CB, blocks, lds, st);
 }
 
-hipError_t qgemv_v2_i4_bf16_r(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st) {
-  return launch_v2<kFmtInt4, kBF16, false>(a, L, CB, blocks, lds, st);
+hipError_t qgemv_v2_i4_bf16_r(const GemvArgs& a, const GemvArgs& b, int na, int L, int CB, int blocks, size_t lds,
+                  hipStream_t st) {
+  return launch_v2<kFmtInt4, kBF16, false>(a, b, na, L, CB, blocks, lds, st);
 }
 
 }  // namespace qm

@@ -92,9 +92,15 @@ inline hipError_t launch_g(const GemvArgs& a, int L, int NB, int blocks, size_t 
 // Pipelined single-token GEMV: the whole x is staged once per block, each
 // wave walks its tiles (grid stride) with unit i+1's weights in flight while
 // unit i is computed, and the first unit's loads are issued before staging.
+// Blocks [0, na) compute matrix `a0`, the others matrix `b0` (a pair of
+// projections of one x in one launch; b0 = a0 and na = gridDim.x for one).
 template <int FMT, int XT, int L, int RU, int CB, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void qgemv_v2_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) void qgemv_v2_kernel(GemvArgs a0, GemvArgs b0, int na) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const bool first = (int)blockIdx.x < na;
+  const GemvArgs a = first ? a0 : b0;
+  const int bid = first ? (int)blockIdx.x : (int)blockIdx.x - na;
+  const int nblk = first ? na : (int)gridDim.x - na;
   constexpr bool SPLIT = (FMT == kFmtInt4 && XT == kF32);
   constexpr int RPW = 64 / L;
   constexpr int TILE = RPW * RU;
@@ -103,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void qgemv_v2_kernel(GemvArgs a) {
   const int kchunks = a.k / Fmt<FMT>::kPerChunk;
   const int ntiles = (a.n + TILE - 1) / TILE;
   const int npasses = (kchunks + L * CB - 1) / (L * CB);
-  const int tstride = gridDim.x * kWaves;
-  const int tile0 = blockIdx.x * kWaves + wave;
+  const int tstride = nblk * kWaves;
+  const int tile0 = bid * kWaves + wave;
   const Mats<1> mt = {{a.q}, {a.s}};
   TileW<1, RU, CB> A, B;
   if (tile0 < ntiles)
@@ -126,21 +132,22 @@ __global__ __launch_bounds__(kThreads) void qgemv_v2_kernel(GemvArgs a) {
 }
 
 template <int FMT, int XT, int L, int CB, bool GROUPED>
-inline hipError_t launch_v2_cb(const GemvArgs& a, int blocks, size_t lds, hipStream_t st) {
+inline hipError_t launch_v2_cb(const GemvArgs& a, const GemvArgs& b, int na, int blocks, size_t lds, hipStream_t st) {
   constexpr int RU = (8 / CB) >= 1 ? (8 / CB >= 8 ? 8 : (8 / CB >= 4 ? 4 : (8 / CB >= 2 ? 2 : 1))) : 1;
-  hipLaunchKernelGGL((qgemv_v2_kernel<FMT, XT, L, RU, CB, GROUPED>), dim3(blocks), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((qgemv_v2_kernel<FMT, XT, L, RU, CB, GROUPED>), dim3(blocks), dim3(kThreads), lds, st, a, b, na);
   return hipGetLastError();
 }
 
 template <int FMT, int XT, bool GROUPED>
-inline hipError_t launch_v2(const GemvArgs& a, int L, int CB, int blocks, size_t lds, hipStream_t st) {
-#define QM_V2L(LL)                                                              \
-  switch (CB) {                                                                 \
-    case 1: return launch_v2_cb<FMT, XT, LL, 1, GROUPED>(a, blocks, lds, st);   \
-    case 2: return launch_v2_cb<FMT, XT, LL, 2, GROUPED>(a, blocks, lds, st);   \
-    case 3: return launch_v2_cb<FMT, XT, LL, 3, GROUPED>(a, blocks, lds, st);   \
-    case 4: return launch_v2_cb<FMT, XT, LL, 4, GROUPED>(a, blocks, lds, st);   \
-    default: return launch_v2_cb<FMT, XT, LL, 8, GROUPED>(a, blocks, lds, st);  \
+inline hipError_t launch_v2(const GemvArgs& a, const GemvArgs& b, int na, int L, int CB, int blocks, size_t lds,
+                            hipStream_t st) {
+#define QM_V2L(LL)                                                                     \
+  switch (CB) {                                                                        \
+    case 1: return launch_v2_cb<FMT, XT, LL, 1, GROUPED>(a, b, na, blocks, lds, st);   \
+    case 2: return launch_v2_cb<FMT, XT, LL, 2, GROUPED>(a, b, na, blocks, lds, st);   \
+    case 3: return launch_v2_cb<FMT, XT, LL, 3, GROUPED>(a, b, na, blocks, lds, st);   \
+    case 4: return launch_v2_cb<FMT, XT, LL, 4, GROUPED>(a, b, na, blocks, lds, st);   \
+    default: return launch_v2_cb<FMT, XT, LL, 8, GROUPED>(a, b, na, blocks, lds, st);  \
   }
   switch (L) {
     case 16: QM_V2L(16)

@@ -69,10 +69,7 @@ int check_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int6
   return QM_OK;
 }
 
-int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_t ldx, float* y, int64_t ldy,
-             void* stream) {
-  int st = check_gemm(w, x, xdt, batch, ldx, y, ldy);
-  if (st != QM_OK || w->n == 0) return st;
+GemvArgs gemv_args(const qm_qmat* w, const void* x, int32_t batch, int64_t ldx, float* y, int64_t ldy) {
   const int g = eff_gs(w->fmt, w->group_size, w->k);
   GemvArgs a{};
   a.q = static_cast<const uint8_t*>(w->q);
@@ -88,8 +85,17 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
   a.ldy = ldy;
   a.nb = batch;
   a.rounds = 1;
+  return a;
+}
+
+int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_t ldx, float* y, int64_t ldy,
+             void* stream) {
+  int st = check_gemm(w, x, xdt, batch, ldx, y, ldy);
+  if (st != QM_OK || w->n == 0) return st;
+  const GemvArgs a = gemv_args(w, x, batch, ldx, y, ldy);
   const int NB = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
-  hipError_t err = launch_qgemv(w->fmt, xdt, g != 0, a, NB, static_cast<hipStream_t>(stream));
+  hipError_t err = launch_qgemv(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, NB,
+                                static_cast<hipStream_t>(stream));
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
 
@@ -192,6 +198,29 @@ const char* qm_strerror(int status) {
 
 int qgemv(const qm_qmat* w, const void* x, int32_t x_dtype, float* y, void* stream) {
   return run_gemm(w, x, x_dtype, 1, w ? w->k : 0, y, w ? w->n : 0, stream);
+}
+
+int qgemv_pair(const qm_qmat* w1, const qm_qmat* w2, const void* x, int32_t x_dtype, float* y1, float* y2,
+               void* stream) {
+  if (!w1 || !w2) return QM_ERR_INVALID;
+  if (w1->k != w2->k) return QM_ERR_INVALID;
+  const int s1 = check_gemm(w1, x, x_dtype, 1, w1->k, y1, w1->n);
+  const int s2 = check_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n);
+  if (s1 != QM_OK) return s1;
+  if (s2 != QM_OK) return s2;
+  if (w1->n == 0 || w2->n == 0) {
+    const int r = run_gemm(w1, x, x_dtype, 1, w1->k, y1, w1->n, stream);
+    return r != QM_OK ? r : run_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n, stream);
+  }
+  const int g1 = eff_gs(w1->fmt, w1->group_size, w1->k), g2 = eff_gs(w2->fmt, w2->group_size, w2->k);
+  if (w1->fmt == w2->fmt && g1 == g2) {
+    const hipError_t err = launch_qgemv_pair(w1->fmt, x_dtype, g1 != 0, gemv_args(w1, x, 1, w1->k, y1, w1->n),
+                                             gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) return QM_OK;
+    if (err != hipErrorNotSupported) return QM_ERR_LAUNCH;
+  }
+  const int r = run_gemm(w1, x, x_dtype, 1, w1->k, y1, w1->n, stream);
+  return r != QM_OK ? r : run_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n, stream);
 }
 
 int qgemm_small(const qm_qmat* w, const void* x, int32_t x_dtype, int32_t batch, int64_t ldx, float* y,

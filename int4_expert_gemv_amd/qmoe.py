@@ -19,7 +19,7 @@ QM_F32, QM_BF16 = 0, 1
 QM_SMALL_MAX, QM_TOPK_MAX, QM_DECODE_MAX_TOKENS = 8, 32, 8
 QM_PATH_AUTO, QM_PATH_DECODE, QM_PATH_PREFILL = 0, 1, 2
 
-EXPORTS = ("qgemv", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
+EXPORTS = ("qgemv", "qgemv_pair", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
            "moe_gate_up", "moe_down", "qm_strerror")
 
 
@@ -48,6 +48,8 @@ def load(path=LIB_PATH):
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.qgemv.argtypes = [ctypes.POINTER(QMat), vp, i32, vp, vp]
     L.qgemv.restype = ctypes.c_int
+    L.qgemv_pair.argtypes = [ctypes.POINTER(QMat), ctypes.POINTER(QMat), vp, i32, vp, vp, vp]
+    L.qgemv_pair.restype = ctypes.c_int
     L.qgemm_small.argtypes = [ctypes.POINTER(QMat), vp, i32, i32, i64, vp, i64, vp]
     L.qgemm_small.restype = ctypes.c_int
     L.moe_expert_ffn_workspace.argtypes = [ctypes.POINTER(Experts), i32, i32]
@@ -109,6 +111,12 @@ def experts(fmt, group_size, gate_q, up_q, down_q, gate_s, up_s, down_s):
 def qgemv(w, x, y, stream=None):
     _check(lib.qgemv(ctypes.byref(w), _ptr(x), _dtype_code(x), _ptr(y), _stream(stream)))
     return y
+
+
+def qgemv_pair(w1, w2, x, y1, y2, stream=None):
+    _check(lib.qgemv_pair(ctypes.byref(w1), ctypes.byref(w2), _ptr(x), _dtype_code(x), _ptr(y1), _ptr(y2),
+                          _stream(stream)))
+    return y1, y2
 
 
 def qgemm_small(w, x, y, stream=None):

@@ -33,7 +33,7 @@ def q():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    assert set(names) == {"qgemv", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
+    assert set(names) == {"qgemv", "qgemv_pair", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
                           "moe_expert_ffn_path", "moe_gate_up", "moe_down", "qm_strerror"}
 
 
@@ -90,6 +90,23 @@ def test_qgemv_bad_dtype_and_nulls(q):
 def test_qgemv_zero_rows_is_a_noop(q):
     m = _mat(q, n=0, qp=0, sp=0)
     assert q.raw_status("qgemv", ctypes.byref(m), None, 1, None, None) == 0
+
+
+def test_qgemv_pair_rejects(q):
+    """Both matrices are validated before anything is enqueued: any invalid
+    one, or two different K, rejects the pair (nothing touches FAKE)."""
+    f = ctypes.c_void_p(FAKE)
+    call = lambda m1, m2, dt=1, x=f: q.raw_status("qgemv_pair", ctypes.byref(m1), ctypes.byref(m2), x, dt, f, f,
+                                                  None)
+    assert call(_mat(q), _mat(q, k=1024)) == -1           # different K
+    assert call(_mat(q), _mat(q, fmt=3)) == -1            # second matrix invalid
+    assert call(_mat(q, sp=0), _mat(q)) == -1             # first matrix invalid
+    assert call(_mat(q), _mat(q, qp=FAKE + 8)) == -2      # second matrix unsupported (alignment)
+    assert call(_mat(q), _mat(q), dt=7) == -1             # bad activation type
+    assert call(_mat(q), _mat(q), x=None) == -1           # null x
+    assert q.raw_status("qgemv_pair", None, ctypes.byref(_mat(q)), f, 1, f, f, None) == -1
+    z = _mat(q, n=0, qp=0, sp=0)
+    assert q.raw_status("qgemv_pair", ctypes.byref(z), ctypes.byref(z), None, 1, None, None, None) == 0
 
 
 def test_qgemm_small_rejects(q):
