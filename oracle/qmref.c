@@ -100,6 +100,19 @@ double qmref_silu(double z) {
 #endif
 }
 
+int qmref_rmsnorm(int n, const double *u, const float *g, double eps, double *out) {
+  if (n < 1 || !u || !out || !(eps >= 0)) return -1;
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += u[i] * u[i];
+#if QMREF_MUTANT == 10
+  const double r = 1.0 / sqrt(ss + eps); /* mutant: sum instead of mean */
+#else
+  const double r = 1.0 / sqrt(ss / n + eps);
+#endif
+  for (int i = 0; i < n; ++i) out[i] = u[i] * r * (g ? (double)g[i] : 1.0);
+  return 0;
+}
+
 int qmref_set_threads(int n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);
@@ -186,6 +199,7 @@ static int check_mat(int fmt, int n, int k, int gs, const void *q, const float *
 
 static double x_at(const void *x, int dt, int64_t i) {
   if (dt == QMREF_BF16) return (double)qmref_bf16_to_f32(((const uint16_t *)x)[i]);
+  if (dt == QMREF_F64) return ((const double *)x)[i];
   return (double)((const float *)x)[i];
 }
 
@@ -193,7 +207,7 @@ int qmref_gemm_small(int fmt, int n, int k, int gs, const uint8_t *q, const floa
                      const void *x, int x_dtype, int batch, int64_t ldx,
                      double *y, int64_t ldy, double *norm) {
   if (check_mat(fmt, n, k, gs, q, scales)) return -1;
-  if (x_dtype != QMREF_F32 && x_dtype != QMREF_BF16) return -1;
+  if (x_dtype != QMREF_F32 && x_dtype != QMREF_BF16 && x_dtype != QMREF_F64) return -1;
   if (batch < 0 || ldx < k || ldy < n || !y || (k > 0 && batch > 0 && !x)) return -1;
   double *xd = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
   if (!xd) return -1;

@@ -41,6 +41,8 @@ extern "C" {
 /* activation dtypes */
 #define QMREF_F32 0  /* IEEE binary32                                         */
 #define QMREF_BF16 1 /* bfloat16 stored as uint16 (upper half of a binary32)  */
+#define QMREF_F64 2  /* IEEE binary64 (gemv / gemm_small only: the input of a
+                        projection that follows another step of the chain)  */
 
 /* moe flags */
 #define QMREF_BF16_ACT 1 /* prefill-precision mode: round x (if fp32) and the
@@ -79,6 +81,13 @@ int qmref_moe_ffn(const qmref_experts *ex, const void *x, int x_dtype, int n_tok
                   double *y, double *h, double *norm);
 
 double qmref_silu(double z);
+
+/* RMS normalisation: out[i] = u[i] / sqrt(mean_j u[j]^2 + eps) * g[i], the
+ * norm of the q latent between the q_a and q_b projections in the colibri
+ * page "Vulkan backend: expert tier + dense + MLA attention on any Vulkan 1.2
+ * GPU" (q-prep chain commit note).  The mean is taken over all n entries in
+ * index order.  g may be NULL (all ones).  n >= 1, eps >= 0.               */
+int qmref_rmsnorm(int n, const double *u, const float *g, double eps, double *out);
 
 /* binary32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN */
 uint16_t qmref_f32_to_bf16(float f);

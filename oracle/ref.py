@@ -24,6 +24,7 @@ FMT_INT4 = 4
 F32 = 0
 BF16 = 1
 BF16_ACT = 1
+F64 = 2
 
 
 def gcc_cmd(out, mutant=0, openmp=True):
@@ -76,6 +77,8 @@ class Oracle:
         L.qmref_weight.argtypes = [i32, i32, i32, vp, vp, i64, i64, ctypes.POINTER(ctypes.c_double)]
         L.qmref_weight.restype = ctypes.c_double
         L.qmref_set_threads.argtypes = [i32]
+        L.qmref_rmsnorm.argtypes = [i32, dp, vp, ctypes.c_double, dp]
+        L.qmref_rmsnorm.restype = i32
         L.qmref_set_threads.restype = i32
         self.L = L
 
@@ -90,7 +93,9 @@ class Oracle:
             return F32
         if x.dtype == np.uint16:
             return BF16
-        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+        if x.dtype == np.float64:
+            return F64
+        raise TypeError("x must be float32, float64 or uint16 (bf16 bits)")
 
     # -- API ----------------------------------------------------------------
     def set_threads(self, n):
@@ -124,6 +129,15 @@ class Oracle:
         if rc:
             raise ValueError("qmref_gemv rejected its arguments")
         return y, nrm
+
+    def rmsnorm(self, u, g=None, eps=0.0):
+        """out = u / sqrt(mean(u^2) + eps) * g, in fp64."""
+        u = np.ascontiguousarray(u, dtype=np.float64)
+        gp = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+        out = np.zeros(u.shape[0], np.float64)
+        if self.L.qmref_rmsnorm(u.shape[0], self._p(u), None if gp is None else self._p(gp), eps, self._p(out)):
+            raise ValueError("qmref_rmsnorm rejected its arguments")
+        return out
 
     def gemm_small(self, fmt, n, k, gs, q, scales, x, want_norm=True):
         """x: [batch][k]; returns y [batch][n] and norm [batch][n]."""

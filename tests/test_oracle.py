@@ -179,7 +179,34 @@ def pin_bruteforce_moe(o, fmt, gs, T=3, E=5, H=128, I=64, k=3, seed=4):
     assert np.all(np.abs(y - yb) <= 1e-12 * nrm), np.max(np.abs(y - yb) / nrm)
 
 
+def pin_rmsnorm(o):
+    """Closed forms of out = u / sqrt(mean(u^2) + eps) * g."""
+    r = np.sqrt(12.5)  # [3, 4]: mean of squares 12.5
+    assert _rel_close(o.rmsnorm([3.0, 4.0]), [3 / r, 4 / r], 1e-15)
+    g = np.arange(1, 8, dtype=np.float32)
+    assert _rel_close(o.rmsnorm(np.full(7, -2.5), g), -g.astype(np.float64), 1e-15)  # constant vector -> sign * g
+    assert _rel_close(o.rmsnorm([1.0, 1.0], np.array([2, -6], np.float32), eps=3.0), [1.0, -3.0], 1e-15)
+    u = np.random.default_rng(11).standard_normal(1536)
+    out = o.rmsnorm(u)
+    assert abs(np.mean(out ** 2) - 1.0) < 1e-12  # unit mean square with eps = 0, g = 1
+    assert _rel_close(o.rmsnorm(u * 1024.0), out, 1e-14)  # scale invariance
+
+
+def pin_f64_input(o):
+    """A float64 activation vector gives what the same values in float32 give."""
+    g = np.random.default_rng(12)
+    nib = g.integers(0, 16, (5, 64))
+    q = bf.pack_nibbles(nib)
+    s = g.uniform(0.5, 2.0, (5, 1)).astype(np.float32)
+    x32 = g.standard_normal(64).astype(np.float32)
+    y32, _ = o.gemv(4, 5, 64, 0, q, s, x32)
+    y64, _ = o.gemv(4, 5, 64, 0, q, s, x32.astype(np.float64))
+    assert np.array_equal(y32, y64)
+
+
 def run_battery(o):
+    pin_rmsnorm(o)
+    pin_f64_input(o)
     pin_hand_gemv(o)
     for gs in (0, 2, 4, 8):
         pin_one_hot(o, gs)
@@ -199,6 +226,11 @@ def run_battery(o):
 
 def test_hand_gemv(oracle):
     pin_hand_gemv(oracle)
+
+
+def test_rmsnorm_closed_forms(oracle):
+    pin_rmsnorm(oracle)
+    pin_f64_input(oracle)
 
 
 @pytest.mark.parametrize("gs", [0, 2, 4, 8, 64])
@@ -446,7 +478,7 @@ def test_moe_bf16_mode_rounds_h(oracle):
 
 MUTANTS = {1: "high nibble first", 2: "offset 7", 3: "wrong group index", 4: "silu sign",
            5: "gate/up swapped", 6: "routing list transposed", 7: "routing weight dropped",
-           8: "bf16 truncation", 9: "int8 unsigned"}
+           8: "bf16 truncation", 9: "int8 unsigned", 10: "rmsnorm sum for mean"}
 
 
 def test_real_oracle_passes_battery(oracle):
