@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "moe_prefill", "gemv", "copy"],
+    p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "moe_prefill", "gemv", "qprep", "copy"],
                    help="copy: a plain 1 GiB device-to-device copy, the reference kernel for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters")
     p.add_argument("--tokens", type=int, default=1)
@@ -388,6 +388,77 @@ def bench_gemv(args):
             **({"separate_calls_us": round(sep_ms * 1e3, 3)} if n2 else {})}
 
 
+def bench_qprep(args):
+    """The q-prep chain: [W_a (6144 -> 2048) + W_kv (6144 -> 576)] x in one
+    launch, RMS norm of the latent, W_b (2048 -> 16384), int4-g64, bf16 x;
+    weight sets in rotation over >= 1 GiB.  Also times the same chain with
+    the norm on the host (a synchronisation and two copies in the middle)."""
+    import torch
+    from int4_expert_gemv_amd import qmoe, synth
+    from oracle import ref
+
+    k, na, nkv, nq, gs = 6144, 2048, 576, 16384, 64
+    row_b = lambda rows, kk: rows * (kk // 2 + 4 * (kk // gs))
+    mb = row_b(na, k) + row_b(nkv, k) + row_b(nq, na)
+    copies = max(1, -(-(1 << 30) // mb))
+    g = np.random.default_rng([args.seed, 91])
+    mats = []
+    for tag, n, kk in ((1, na, k), (2, nkv, k), (3, nq, na)):
+        qw, sc = synth.quant_matrix(np.random.default_rng([args.seed, 91, tag]), 4, n, kk, gs)
+        mats.append(((4, n, kk, gs, qw, sc), [qmoe.qmat(4, dev(qw), dev(sc), n, kk, gs) for _ in range(copies)]))
+    gw_h = (1.0 + 0.1 * g.standard_normal(na)).astype(np.float32)
+    gw = dev(gw_h)
+    eps = 1e-6
+    x_h = synth.activations(g, (k,), "bf16")
+    x = dev(x_h)
+    u = torch.empty(na, device="cuda")
+    kv = torch.empty(nkv, device="cuda")
+    qo = torch.empty(nq, device="cuda")
+
+    def chain(i):
+        qmoe.qgemv_norm_chain(mats[0][1][i], mats[1][1][i], gw, eps, mats[2][1][i], x, u, kv, qo)
+
+    def host_norm(i):
+        qmoe.qgemv_pair(mats[0][1][i], mats[1][1][i], x, u, kv)
+        uh = u.cpu().numpy()
+        un = uh / np.sqrt(np.mean(uh * uh) + eps) * gw_h
+        u.copy_(torch.from_numpy(un.astype(np.float32)))
+        qmoe.qgemv(mats[2][1][i], u, qo)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for j in range(args.steps):
+            fn(j % copies)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    host_ms = timed(host_norm)
+    ms = timed(chain)
+    o = ref.oracle()
+    ur, _ = o.gemv(*mats[0][0], x_h)
+    un = o.rmsnorm(ur, gw_h, eps)
+    yq, nrq = o.gemv(*mats[2][0], un)
+    yk, nrk = o.gemv(*mats[1][0], x_h)
+    err = max(ref.max_norm_err(qo.cpu().numpy(), yq, nrq), ref.max_norm_err(kv.cpu().numpy(), yk, nrk))
+    byts = mb + k * 2 + (na + nkv + nq) * 4 + na * 4
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"metric": "achieved HBM GB/s for the q-prep chain (pair GEMV, RMS norm, GEMV)", "value": round(gbs, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "us_per_call": round(ms * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "qgemv_norm_chain: %d -> (%d, %d), rmsnorm, %d -> %d, int4-g64, bf16 x, "
+                                   "%d weight sets in rotation" % (k, na, nkv, na, nq, copies)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,
+            "norm_on_host_us": round(host_ms * 1e3, 3)}
+
+
 def bench_copy(args):
     """A plain device copy of known size (1 GiB read + 1 GiB written per launch)."""
     import torch
@@ -425,6 +496,8 @@ def main():
         out = bench_moe(args, 256, 2048, 512)
     elif args.config == "moe_prefill":
         out = bench_prefill(args)
+    elif args.config == "qprep":
+        out = bench_qprep(args)
     elif args.config == "copy":
         out = bench_copy(args)
     else:

@@ -117,6 +117,20 @@ QM_API int qgemv(const qm_qmat *w, const void *x, int32_t x_dtype, float *y, voi
 QM_API int qgemv_pair(const qm_qmat *w1, const qm_qmat *w2, const void *x, int32_t x_dtype, float *y1, float *y2,
                       void *stream);
 
+/* The q-prep chain: u = W_a x and kv = W_kv x (one qgemv_pair launch), then
+ * u is RMS-normalised in place, u[i] <- u[i] / sqrt(mean u^2 + eps) * g[i],
+ * then q = W_b u -- three launches on the stream and no host
+ * synchronisation.  [V: the q-prep chain commit note -- q_a + kv_a, the
+ * latent norm and q_b recorded as one GPU sequence]
+ * w_kv->k == w_a->k, w_b->k == w_a->n >= 1.  x: device, w_a->k elements of
+ * x_dtype.  u: device fp32 [w_a->n], 16-byte aligned (receives the
+ * normalised latent; it is also q_b's input).  kv: device fp32 [w_kv->n].
+ * q: device fp32 [w_b->n].  norm_w: device fp32 [w_a->n], or NULL for ones.
+ * eps >= 0.  All three matrices are validated before anything is enqueued. */
+QM_API int qgemv_norm_chain(const qm_qmat *w_a, const qm_qmat *w_kv, const float *norm_w, float eps,
+                            const qm_qmat *w_b, const void *x, int32_t x_dtype, float *u, float *kv, float *q,
+                            void *stream);
+
 /* Y[t][r] = sum_c W[r][c] * X[t][c] for t < batch, reading W once for all
  * t.  [V: qmatmul.comp note -- the S-token batch of the same GEMV]
  * x: device [batch][ldx] (ldx >= k, ldx*elemsize a multiple of 16 bytes).

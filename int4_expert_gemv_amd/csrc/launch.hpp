@@ -57,6 +57,8 @@ hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a, int N
 // pipelined kernel; hipErrorNotSupported when that kernel does not take them
 // (the caller then launches them one by one).
 hipError_t launch_qgemv_pair(int fmt, int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st);
+// u[i] <- u[i] / sqrt(mean u^2 + eps) * g[i] in place, one workgroup.
+hipError_t launch_rmsnorm(float* u, const float* g, int n, float eps, hipStream_t st);
 hipError_t launch_fill_zero(float* y, int64_t n, int64_t ld, int rows, hipStream_t st);
 
 // per-instantiation launchers (qgemv_*.hip): grouped (_g) or row-scaled (_r)

@@ -223,6 +223,20 @@ int qgemv_pair(const qm_qmat* w1, const qm_qmat* w2, const void* x, int32_t x_dt
   return r != QM_OK ? r : run_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n, stream);
 }
 
+int qgemv_norm_chain(const qm_qmat* w_a, const qm_qmat* w_kv, const float* norm_w, float eps, const qm_qmat* w_b,
+                     const void* x, int32_t x_dtype, float* u, float* kv, float* q, void* stream) {
+  if (!w_a || !w_kv || !w_b) return QM_ERR_INVALID;
+  if (w_a->k != w_kv->k || w_b->k != w_a->n || w_a->n < 1 || !(eps >= 0.f)) return QM_ERR_INVALID;
+  int st = check_gemm(w_a, x, x_dtype, 1, w_a->k, u, w_a->n);
+  if (st == QM_OK) st = check_gemm(w_kv, x, x_dtype, 1, w_kv->k, kv, w_kv->n);
+  if (st == QM_OK) st = check_gemm(w_b, u, QM_F32, 1, w_b->k, q, w_b->n);
+  if (st != QM_OK) return st;
+  st = qgemv_pair(w_a, w_kv, x, x_dtype, u, kv, stream);
+  if (st != QM_OK) return st;
+  if (launch_rmsnorm(u, norm_w, w_a->n, eps, static_cast<hipStream_t>(stream)) != hipSuccess) return QM_ERR_LAUNCH;
+  return run_gemm(w_b, u, QM_F32, 1, w_b->k, q, w_b->n, stream);
+}
+
 int qgemm_small(const qm_qmat* w, const void* x, int32_t x_dtype, int32_t batch, int64_t ldx, float* y,
                 int64_t ldy, void* stream) {
   return run_gemm(w, x, x_dtype, batch, ldx, y, ldy, stream);

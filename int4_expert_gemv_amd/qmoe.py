@@ -19,7 +19,7 @@ QM_F32, QM_BF16 = 0, 1
 QM_SMALL_MAX, QM_TOPK_MAX, QM_DECODE_MAX_TOKENS = 8, 32, 8
 QM_PATH_AUTO, QM_PATH_DECODE, QM_PATH_PREFILL = 0, 1, 2
 
-EXPORTS = ("qgemv", "qgemv_pair", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
+EXPORTS = ("qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
            "moe_gate_up", "moe_down", "qm_strerror")
 
 
@@ -50,6 +50,9 @@ def load(path=LIB_PATH):
     L.qgemv.restype = ctypes.c_int
     L.qgemv_pair.argtypes = [ctypes.POINTER(QMat), ctypes.POINTER(QMat), vp, i32, vp, vp, vp]
     L.qgemv_pair.restype = ctypes.c_int
+    L.qgemv_norm_chain.argtypes = [ctypes.POINTER(QMat), ctypes.POINTER(QMat), vp, ctypes.c_float,
+                                   ctypes.POINTER(QMat), vp, i32, vp, vp, vp, vp]
+    L.qgemv_norm_chain.restype = ctypes.c_int
     L.qgemm_small.argtypes = [ctypes.POINTER(QMat), vp, i32, i32, i64, vp, i64, vp]
     L.qgemm_small.restype = ctypes.c_int
     L.moe_expert_ffn_workspace.argtypes = [ctypes.POINTER(Experts), i32, i32]
@@ -117,6 +120,14 @@ def qgemv_pair(w1, w2, x, y1, y2, stream=None):
     _check(lib.qgemv_pair(ctypes.byref(w1), ctypes.byref(w2), _ptr(x), _dtype_code(x), _ptr(y1), _ptr(y2),
                           _stream(stream)))
     return y1, y2
+
+
+def qgemv_norm_chain(w_a, w_kv, norm_w, eps, w_b, x, u, kv, q, stream=None):
+    """u = rmsnorm(W_a x) * norm_w (norm_w None: ones), kv = W_kv x, q = W_b u."""
+    _check(lib.qgemv_norm_chain(ctypes.byref(w_a), ctypes.byref(w_kv), None if norm_w is None else _ptr(norm_w),
+                                eps, ctypes.byref(w_b), _ptr(x), _dtype_code(x), _ptr(u), _ptr(kv), _ptr(q),
+                                _stream(stream)))
+    return u, kv, q
 
 
 def qgemm_small(w, x, y, stream=None):

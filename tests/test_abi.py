@@ -33,7 +33,7 @@ def q():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    assert set(names) == {"qgemv", "qgemv_pair", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
+    assert set(names) == {"qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
                           "moe_expert_ffn_path", "moe_gate_up", "moe_down", "qm_strerror"}
 
 
@@ -107,6 +107,26 @@ def test_qgemv_pair_rejects(q):
     assert q.raw_status("qgemv_pair", None, ctypes.byref(_mat(q)), f, 1, f, f, None) == -1
     z = _mat(q, n=0, qp=0, sp=0)
     assert q.raw_status("qgemv_pair", ctypes.byref(z), ctypes.byref(z), None, 1, None, None, None) == 0
+
+
+def test_qgemv_norm_chain_rejects(q):
+    """Shape links between the three matrices and every operand are checked
+    before anything is enqueued."""
+    f = ctypes.c_void_p(FAKE)
+
+    def call(wa, wkv, wb, eps=1e-6, dt=1, u=FAKE):
+        return q.raw_status("qgemv_norm_chain", ctypes.byref(wa), ctypes.byref(wkv), f, ctypes.c_float(eps),
+                            ctypes.byref(wb), f, dt, ctypes.c_void_p(u), f, f, None)
+
+    a, kv, b = _mat(q, n=64, k=512), _mat(q, n=32, k=512), _mat(q, n=128, k=64)
+    assert call(a, kv, _mat(q, n=128, k=128)) == -1       # q_b's K is not q_a's N
+    assert call(a, _mat(q, n=32, k=1024), b) == -1        # kv_a reads another x length
+    assert call(a, kv, b, eps=-1.0) == -1                 # negative eps
+    assert call(a, kv, b, dt=5) == -1                     # bad activation type
+    assert call(a, kv, _mat(q, n=128, k=64, sp=0)) == -1  # q_b invalid
+    assert call(a, kv, b, u=FAKE + 4) == -2               # latent not 16-byte aligned (it is q_b's input)
+    assert q.raw_status("qgemv_norm_chain", None, ctypes.byref(kv), f, ctypes.c_float(0), ctypes.byref(b), f, 1, f,
+                        f, f, None) == -1
 
 
 def test_qgemm_small_rejects(q):
