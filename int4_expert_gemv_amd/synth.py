@@ -17,6 +17,7 @@ import torch
 
 FMT_INT8_ROW = 1
 FMT_INT4 = 4
+FMT_INT3 = 5
 
 _T_GATE, _T_UP, _T_DOWN = 1, 2, 3
 _T_Q, _T_S = 0, 1
@@ -40,6 +41,10 @@ def quant_matrix(g, fmt, n, k, gs, scale_lo=0.005, scale_hi=0.02):
     elif fmt == FMT_INT8_ROW:
         q = g.integers(-127, 128, size=(n, k), dtype=np.int8)
         s = uniform_f32(g, (n, 1), scale_lo, scale_hi)
+    elif fmt == FMT_INT3:  # any bit pattern is a valid int3 group (24 bytes per 64 inputs)
+        ng = (k + 63) // 64
+        q = g.integers(0, 256, size=(n, ng * 24), dtype=np.uint8)
+        s = uniform_f32(g, (n, ng), scale_lo, scale_hi)
     else:
         raise ValueError(fmt)
     return q, s

@@ -15,7 +15,12 @@
  *        down projection, outputs combined by weighted accumulation;
  *      - commit note "fmt=4 grouped scales": one scale per gs consecutive
  *        inputs of a row, applied to the partial dot of that group; the
- *        per-row multiply is skipped.
+ *        per-row multiply is skipped;
+ *      - the int3 commit notes ("fmt 5"): a 24-byte two-plane group per 64
+ *        inputs, the low plane as 16-value words, the high plane shifted so a
+ *        word's bits start at bit 0, one scale per group;
+ *      - the q-prep chain commit note: an RMS norm of the q latent between
+ *        the q_a and q_b projections.
  *  [Q] "qwen36: Vulkan expert tier, and staged device-local uploads": int4-gs64
  *      arrives as fmt 4 / group 64 at half a byte per element; int8 experts
  *      arrive as fmt 1; the take path accumulates each expert output with its
@@ -26,6 +31,11 @@
  *  - scales are fp32 laid out [row][group], groups run along the inputs and
  *    restart every row, the last group of a row may be shorter (ceil);
  *  - int8 is plain two's complement with no zero point;
+ *  - int3: value i of a group sits at bits 2 (i % 16) of the little-endian
+ *    low word i / 16 and at bit i of the little-endian high word; the
+ *    decoded weight is value - 4 (offset-binary, as int4's nibble - 8);
+ *  - the q-latent norm is u / sqrt(mean u^2 + eps) times a per-element
+ *    weight;
  *  - the routing weight multiplies each expert's down output and the slots of
  *    a token are summed in slot order with no renormalisation;
  *  - silu(z) = z / (1 + exp(-z)).
@@ -125,11 +135,22 @@ int qmref_set_threads(int n) {
 
 /* ---- weight decode -------------------------------------------------------- */
 
-static int64_t row_bytes(int fmt, int k) { return fmt == QMREF_FMT_INT4 ? (int64_t)k / 2 : (int64_t)k; }
+static int64_t row_bytes(int fmt, int k) {
+  if (fmt == QMREF_FMT_INT3) return ((int64_t)k + 63) / 64 * 24;
+  return fmt == QMREF_FMT_INT4 ? (int64_t)k / 2 : (int64_t)k;
+}
 
 static int64_t n_groups(int fmt, int k, int gs) {
+  if (fmt == QMREF_FMT_INT3) return ((int64_t)k + 63) / 64;
   if (fmt != QMREF_FMT_INT4 || gs <= 0) return 1;
   return ((int64_t)k + gs - 1) / gs;
+}
+
+/* little-endian reads, independent of the host's byte order */
+static uint64_t le_bytes(const uint8_t *p, int n) {
+  uint64_t v = 0;
+  for (int i = n - 1; i >= 0; --i) v = (v << 8) | p[i];
+  return v;
 }
 
 double qmref_weight(int fmt, int k, int gs, const uint8_t *q, const float *scales,
@@ -137,7 +158,22 @@ double qmref_weight(int fmt, int k, int gs, const uint8_t *q, const float *scale
   const uint8_t *r = q + row * row_bytes(fmt, k);
   double v;
   int64_t g = 0;
-  if (fmt == QMREF_FMT_INT4) {
+  if (fmt == QMREF_FMT_INT3) {
+    /* group g = col / 64 occupies bytes [24 g, 24 g + 24) of the row: low
+     * parts of values 16 j .. 16 j + 15 in the 32-bit word j (value i at bits
+     * 2 (i % 16), 2 (i % 16) + 1), high bits of values 0..63 in the 64-bit word
+     * at byte 16 (value i at bit i) */
+    const uint8_t *grp = r + (col / 64) * 24;
+    const int i = (int)(col % 64);
+    const int lo = (int)((le_bytes(grp + 4 * (i / 16), 4) >> (2 * (i % 16))) & 3u);
+    const int hi = (int)((le_bytes(grp + 16, 8) >> i) & 1u);
+#if QMREF_MUTANT == 11
+    v = (double)((lo | (hi << 2)) - 3); /* mutant: wrong int3 offset */
+#else
+    v = (double)((lo | (hi << 2)) - 4);
+#endif
+    g = col / 64;
+  } else if (fmt == QMREF_FMT_INT4) {
     uint8_t byte = r[col >> 1];
 #if QMREF_MUTANT == 1
     int nib = (col & 1) ? (byte & 0xF) : (byte >> 4); /* mutant: high nibble first */
@@ -168,7 +204,7 @@ double qmref_weight(int fmt, int k, int gs, const uint8_t *q, const float *scale
 static void gemv_d(int fmt, int n, int k, int gs, const uint8_t *q, const float *scales,
                    const double *x, double *y, double *norm) {
   int64_t G = n_groups(fmt, k, gs);
-  int64_t glen = (fmt == QMREF_FMT_INT4 && gs > 0) ? gs : k;
+  int64_t glen = fmt == QMREF_FMT_INT3 ? 64 : ((fmt == QMREF_FMT_INT4 && gs > 0) ? gs : k);
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static)
 #endif
@@ -190,8 +226,9 @@ static void gemv_d(int fmt, int n, int k, int gs, const uint8_t *q, const float 
 }
 
 static int check_mat(int fmt, int n, int k, int gs, const void *q, const float *scales) {
-  if (fmt != QMREF_FMT_INT4 && fmt != QMREF_FMT_INT8_ROW) return -1;
+  if (fmt != QMREF_FMT_INT4 && fmt != QMREF_FMT_INT8_ROW && fmt != QMREF_FMT_INT3) return -1;
   if (n < 0 || k < 0 || gs < 0) return -1;
+  if (fmt == QMREF_FMT_INT3 && gs != 64) return -1;
   if (fmt == QMREF_FMT_INT4 && (k & 1)) return -1;
   if ((n > 0 && k > 0) && (!q || !scales)) return -1;
   return 0;

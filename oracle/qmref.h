@@ -37,6 +37,10 @@ extern "C" {
 /* weight formats */
 #define QMREF_FMT_INT8_ROW 1 /* int8 two's complement, one fp32 scale per row */
 #define QMREF_FMT_INT4 4     /* int4 nibble-8, one fp32 scale per gs inputs   */
+#define QMREF_FMT_INT3 5     /* int3 in two bit planes per 64 inputs (24 bytes:
+                                four 32-bit words of 2-bit low parts, 16 values
+                                each, then one 64-bit word of high bits), value
+                                - 4, one fp32 scale per 64 inputs (gs = 64)   */
 
 /* activation dtypes */
 #define QMREF_F32 0  /* IEEE binary32                                         */

@@ -21,6 +21,7 @@ LIB = os.path.join(HERE, "libqmref.so")
 
 FMT_INT8_ROW = 1
 FMT_INT4 = 4
+FMT_INT3 = 5
 F32 = 0
 BF16 = 1
 BF16_ACT = 1

@@ -204,7 +204,54 @@ def pin_f64_input(o):
     assert np.array_equal(y32, y64)
 
 
+def pack_int3(vals):
+    """Test-side packer for the int3 two-plane layout (independent of the
+    generators): per 64-group, four little-endian 32-bit words of 2-bit low
+    parts (value i of the group at bits 2 (i % 16) of word i // 16), then a
+    64-bit word of high bits (value i at bit i); a ragged last group is
+    padded with zeros."""
+    vals = np.asarray(vals)
+    n, k = vals.shape
+    G = (k + 63) // 64
+    out = np.zeros((n, G * 24), np.uint8)
+    for r in range(n):
+        for g in range(G):
+            lo, hi = [0, 0, 0, 0], 0
+            for i in range(64):
+                c = 64 * g + i
+                v = int(vals[r, c]) if c < k else 0
+                lo[i // 16] |= (v & 3) << (2 * (i % 16))
+                hi |= ((v >> 2) & 1) << i
+            raw = b"".join(w.to_bytes(4, "little") for w in lo) + hi.to_bytes(8, "little")
+            out[r, 24 * g:24 * g + 24] = np.frombuffer(raw, np.uint8)
+    return out
+
+
+def pin_int3(o):
+    """One-hot columns (every bit position class, a ragged tail group) give
+    (v - 4) * scale exactly; an int3 matrix equals the int4-g64 matrix with
+    nibbles v + 4 and the same scales."""
+    g = np.random.default_rng(13)
+    n, k = 3, 96
+    vals = g.integers(0, 8, (n, k))
+    s = g.uniform(0.5, 2.0, (n, 2)).astype(np.float32)
+    q3 = pack_int3(vals)
+    for c in (0, 1, 7, 15, 16, 30, 31, 47, 48, 63, 64, 70, 95):
+        x = np.zeros(k, np.float32)
+        x[c] = 1.0
+        y, _ = o.gemv(5, n, k, 64, q3, s, x)
+        assert np.array_equal(y, (vals[:, c] - 4) * s[:, c // 64].astype(np.float64)), c
+    k2 = 256
+    vals2 = g.integers(0, 8, (n, k2))
+    s2 = g.uniform(0.5, 2.0, (n, 4)).astype(np.float32)
+    x2 = g.standard_normal(k2).astype(np.float32)
+    y3, n3 = o.gemv(5, n, k2, 64, pack_int3(vals2), s2, x2)
+    y4, n4 = o.gemv(4, n, k2, 64, bf.pack_nibbles(vals2 + 4), s2, x2)
+    assert np.array_equal(y3, y4) and np.array_equal(n3, n4)
+
+
 def run_battery(o):
+    pin_int3(o)
     pin_rmsnorm(o)
     pin_f64_input(o)
     pin_hand_gemv(o)
@@ -226,6 +273,10 @@ def run_battery(o):
 
 def test_hand_gemv(oracle):
     pin_hand_gemv(oracle)
+
+
+def test_int3_decode(oracle):
+    pin_int3(oracle)
 
 
 def test_rmsnorm_closed_forms(oracle):
@@ -478,7 +529,7 @@ def test_moe_bf16_mode_rounds_h(oracle):
 
 MUTANTS = {1: "high nibble first", 2: "offset 7", 3: "wrong group index", 4: "silu sign",
            5: "gate/up swapped", 6: "routing list transposed", 7: "routing weight dropped",
-           8: "bf16 truncation", 9: "int8 unsigned", 10: "rmsnorm sum for mean"}
+           8: "bf16 truncation", 9: "int8 unsigned", 10: "rmsnorm sum for mean", 11: "int3 offset 3"}
 
 
 def test_real_oracle_passes_battery(oracle):
