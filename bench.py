@@ -44,7 +44,7 @@ def parse():
                         "the value is the number of rotating copies of it (one per layer of a model)")
     p.add_argument("--batch", type=int, default=1, help="gemv: activations per weight read (qgemm_small when > 1)")
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
-    p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row")
+    p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row, 5 = int3-g64 two-plane")
     p.add_argument("--n", type=int, default=6144)
     p.add_argument("--pair", type=int, default=0,
                    help="gemv: rows of a second matrix of the same x and format, run with qgemv_pair "
@@ -320,9 +320,15 @@ def bench_gemv(args):
     from int4_expert_gemv_amd import qmoe, synth
     from oracle import ref
 
-    fmt, n, k, gs, B = args.fmt, args.n, args.k, (args.gs if args.fmt == 4 else 0), args.batch
+    fmt, n, k, B = args.fmt, args.n, args.k, args.batch
+    gs = args.gs if fmt == 4 else (64 if fmt == 5 else 0)
     n2 = args.pair if B == 1 else 0
-    row_b = lambda rows: (rows * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else rows * (k + 4)
+
+    def row_b(rows):
+        if fmt == 5:  # int3-g64: 24 bytes + one fp32 scale per 64 inputs
+            return rows * ((k + 63) // 64) * (24 + 4)
+        return (rows * (k // 2 + 4 * (k // gs if gs else 1))) if fmt == 4 else rows * (k + 4)
+
     mb = row_b(n) + row_b(n2)
     copies = max(1, -(-(1 << 30) // mb))  # at least 1 GiB of distinct weights in rotation
     g = np.random.default_rng([args.seed, 77])
@@ -375,7 +381,7 @@ def bench_gemv(args):
         err = max(err, ref.max_norm_err(y2.cpu().numpy(), yr, nr))
     byts = mb + B * k * 2 + B * (n + n2) * 4
     gbs = byts / (ms * 1e-3) / 1e9
-    wname = ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else "int8-row"
+    wname = ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else ("int3-g64" if fmt == 5 else "int8-row")
     return {"metric": "achieved HBM GB/s for quantized GEMV", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 3),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",

@@ -39,6 +39,15 @@
  *  - QM_FMT_INT8_ROW: element (r, c) = (int8_t)q[r*k + c] times scale[r]
  *    (two's complement, no zero point) [V: qmatmul.comp note, Q: fmt 1].
  *    group_size must be 0.
+ *  - QM_FMT_INT3 (int3-g64, two bit planes): each 64 inputs of a row take 24
+ *    bytes -- four 32-bit words of 2-bit low parts (16 values per word), then
+ *    a 64-bit word of high bits -- with one fp32 scale per group, [n][ceil(k/64)]
+ *    [V: the int3 commit notes, 24 bytes per 64-group].  Reading of the bit
+ *    order: value i of a group at bits 2 (i % 16) of little-endian low word
+ *    i / 16 and at bit i of the little-endian high word; element = value - 4.
+ *    Rows are ceil(k/64) * 24 bytes (a ragged last group is padded).
+ *    group_size must be 64.  qgemv, qgemv_pair and qgemm_small with batch 1
+ *    take it (k <= 16384); the expert FFN does not (QM_ERR_UNSUPPORTED).
  *  Value = element * its scale.  Accumulation on the GPU is fp32.
  *
  * Shape limits of the GPU path (QM_ERR_UNSUPPORTED otherwise): int4 needs
@@ -69,7 +78,7 @@ typedef enum {
   QM_ERR_LAUNCH = -4       /* a HIP launch failed */
 } qm_status;
 
-typedef enum { QM_FMT_INT8_ROW = 1, QM_FMT_INT4 = 4 } qm_fmt;
+typedef enum { QM_FMT_INT8_ROW = 1, QM_FMT_INT4 = 4, QM_FMT_INT3 = 5 } qm_fmt;
 typedef enum { QM_F32 = 0, QM_BF16 = 1 } qm_dtype;
 
 enum {

@@ -57,6 +57,11 @@ hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a, int N
 // pipelined kernel; hipErrorNotSupported when that kernel does not take them
 // (the caller then launches them one by one).
 hipError_t launch_qgemv_pair(int fmt, int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st);
+// int3-g64 GEMV (fmt 5): y = W x for k <= kI3KMax; LDS bytes it stages.
+constexpr int kI3KMax = 16384;
+size_t qgemv_i3_lds(int k, int xdt);
+hipError_t launch_qgemv_i3(const uint8_t* q, const float* sc, const void* x, int xdt, float* y, int n, int k,
+                           hipStream_t st);
 // u[i] <- u[i] / sqrt(mean u^2 + eps) * g[i] in place, one workgroup.
 hipError_t launch_rmsnorm(float* u, const float* g, int n, float eps, hipStream_t st);
 hipError_t launch_fill_zero(float* y, int64_t n, int64_t ld, int rows, hipStream_t st);

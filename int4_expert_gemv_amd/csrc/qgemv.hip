@@ -95,6 +95,7 @@ hipError_t launch_qgemv(int fmt, int xdt, bool grouped, const GemvArgs& a0, int 
 
 hipError_t launch_qgemv_pair(int fmt, int xdt, bool grouped, const GemvArgs& a0, const GemvArgs& b0, hipStream_t st) {
   GemvArgs a = a0, b = b0;
+  if (fmt != kFmtInt4 && fmt != kFmtInt8) return hipErrorNotSupported;
   const int kchunks = a.k / (fmt == kFmtInt4 ? 32 : 16);
   const int L = lanes_per_row(kchunks);
   if (xdt != kBF16 || L < 16 || a.k != b.k || stage_bytes(fmt, xdt, 1, kchunks) > (size_t)kLdsBudget)

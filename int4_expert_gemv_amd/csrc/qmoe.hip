@@ -22,11 +22,19 @@ int ilog2(int v) {
 }
 
 // Effective group size: 0 means one scale per row.
-int eff_gs(int fmt, int gs, int k) { return (fmt == QM_FMT_INT4 && gs > 0 && gs < k) ? gs : 0; }
+int eff_gs(int fmt, int gs, int k) {
+  if (fmt == QM_FMT_INT3) return 64;
+  return (fmt == QM_FMT_INT4 && gs > 0 && gs < k) ? gs : 0;
+}
 
 // Shape checks for one n x k matrix in (fmt, gs).  Returns a qm_status.
 int check_shape(int fmt, int n, int k, int gs) {
-  if (fmt != QM_FMT_INT4 && fmt != QM_FMT_INT8_ROW) return QM_ERR_INVALID;
+  if (fmt != QM_FMT_INT4 && fmt != QM_FMT_INT8_ROW && fmt != QM_FMT_INT3) return QM_ERR_INVALID;
+  if (fmt == QM_FMT_INT3) {  // int3-g64: group size 64 only, rows staged whole
+    if (n < 0 || k < 0 || gs != 64) return QM_ERR_INVALID;
+    if (k == 0 || k > kI3KMax || k % 32) return QM_ERR_UNSUPPORTED;
+    return QM_OK;
+  }
   if (n < 0 || k < 0 || gs < 0) return QM_ERR_INVALID;
   if (fmt == QM_FMT_INT4 && (k & 1)) return QM_ERR_INVALID;
   if (fmt == QM_FMT_INT8_ROW && gs != 0) return QM_ERR_INVALID;
@@ -42,9 +50,13 @@ int check_shape(int fmt, int n, int k, int gs) {
   return QM_OK;
 }
 
-int64_t row_bytes(int fmt, int k) { return fmt == QM_FMT_INT4 ? (int64_t)k / 2 : (int64_t)k; }
+int64_t row_bytes(int fmt, int k) {
+  if (fmt == QM_FMT_INT3) return ((int64_t)k + 63) / 64 * 24;
+  return fmt == QM_FMT_INT4 ? (int64_t)k / 2 : (int64_t)k;
+}
 
 int groups(int fmt, int gs, int k) {
+  if (fmt == QM_FMT_INT3) return (k + 63) / 64;
   const int g = eff_gs(fmt, gs, k);
   return g ? k / g : 1;
 }
@@ -63,6 +75,7 @@ int check_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int6
   if (ldx < w->k || ldy < w->n) return QM_ERR_INVALID;
   if (st != QM_OK) return st;
   if (batch > QM_SMALL_MAX) return QM_ERR_UNSUPPORTED;
+  if (w->fmt == QM_FMT_INT3 && batch > 1) return QM_ERR_UNSUPPORTED;  // one token per weight read
   if (!aligned(w->q, 16) || !aligned(x, 16) || !aligned(w->scales, 4) || !aligned(y, 4))
     return QM_ERR_UNSUPPORTED;
   if ((ldx * xsize(xdt)) % 16) return QM_ERR_UNSUPPORTED;
@@ -92,6 +105,11 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
              void* stream) {
   int st = check_gemm(w, x, xdt, batch, ldx, y, ldy);
   if (st != QM_OK || w->n == 0) return st;
+  if (w->fmt == QM_FMT_INT3) {
+    const hipError_t e3 = launch_qgemv_i3(static_cast<const uint8_t*>(w->q), w->scales, x, xdt, y, w->n, w->k,
+                                          static_cast<hipStream_t>(stream));
+    return e3 == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   const GemvArgs a = gemv_args(w, x, batch, ldx, y, ldy);
   const int NB = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
   hipError_t err = launch_qgemv(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, NB,
@@ -104,6 +122,7 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
 // Shapes, format and group size only (no pointers).
 bool moe_shape_ok(const qm_experts* ex) {
   if (ex->n_experts < 1 || ex->hidden < 1 || ex->inter < 1) return false;
+  if (ex->fmt == QM_FMT_INT3) return false;  // the expert kernels take int4 and int8
   if (check_shape(ex->fmt, ex->inter, ex->hidden, ex->group_size) != QM_OK) return false;
   if (check_shape(ex->fmt, ex->hidden, ex->inter, ex->group_size) != QM_OK) return false;
   const int gh = eff_gs(ex->fmt, ex->group_size, ex->hidden);
@@ -120,6 +139,7 @@ int check_experts(const qm_experts* ex) {
   if (a != QM_OK) return a;
   if (b != QM_OK) return b;
   if (ex->hidden < 1 || ex->inter < 1) return QM_ERR_UNSUPPORTED;
+  if (ex->fmt == QM_FMT_INT3) return QM_ERR_UNSUPPORTED;
   const void* q[3] = {ex->gate_q, ex->up_q, ex->down_q};
   const void* s[3] = {ex->gate_s, ex->up_s, ex->down_s};
   for (int i = 0; i < 3; ++i)

@@ -129,6 +129,21 @@ def test_qgemv_norm_chain_rejects(q):
                         f, f, None) == -1
 
 
+def test_int3_limits(q):
+    """int3-g64: group size 64 only, k <= 16384, one token per weight read,
+    not an expert format."""
+    f = ctypes.c_void_p(FAKE)
+    st = lambda m: q.raw_status("qgemv", ctypes.byref(m), f, 1, f, None)
+    assert st(_mat(q, fmt=5, gs=0)) == -1                  # int3 needs group size 64
+    assert st(_mat(q, fmt=5, gs=128)) == -1
+    assert st(_mat(q, fmt=5, k=16416)) == -2               # k above the staged maximum
+    assert st(_mat(q, fmt=5, k=80)) == -2                  # k not a multiple of 32
+    m = _mat(q, fmt=5)
+    assert q.raw_status("qgemm_small", ctypes.byref(m), f, 1, 2, ctypes.c_int64(512), f, ctypes.c_int64(64),
+                        None) == -2                        # batch > 1
+    assert _moe(q, _experts(q, fmt=5, gs=64)) == -2        # expert FFN takes int4 / int8 only
+
+
 def test_qgemm_small_rejects(q):
     m = _mat(q)
     f = ctypes.c_void_p(FAKE)
