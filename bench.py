@@ -88,7 +88,8 @@ def counter_traffic(name):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("source_digest") != hipbuild.source_digest() or "traffic_bytes_per_launch" not in kv:
+    if kv.get("source_digest") != hipbuild.source_digest(hipbuild.DECODE_SOURCES) or \
+            "traffic_bytes_per_launch" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 

@@ -26,14 +26,27 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def source_digest():
-    """sha256 over every kernel source, header and the public header (in name
-    order): a hardware-counter summary taken from a build is valid only while
-    this digest is unchanged."""
+# The sources the single-token decode kernels are built from (the fused
+# gate+up kernel whose counters the bench reports, and the down kernel).
+DECODE_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_t1_lds.hpp", "moe_t1_impl.hpp",
+                  "moe_decode_impl.hpp", "moe_decode.hip", "moe_decode_i4_bf16.hip", "qmoe.hip")
+
+
+# The sources of the prefill kernels.
+PREFILL_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_prefill.hip", "qmoe.hip")
+
+
+def source_digest(names=None):
+    """sha256 over kernel sources and the public header (in name order), with
+    the compile flags: a hardware-counter summary taken from a build is valid
+    only while this digest is unchanged.  `names` limits it to those files of
+    the kernel directory (the ones a given kernel is built from); default all."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")) +
-                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    srcs = glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
+    if names is not None:
+        srcs = [f for f in srcs if os.path.basename(f) in names]
+    files = sorted(srcs + glob.glob(os.path.join(ROOT, "include", "*.h")))
     for f in files:
         h.update(os.path.basename(f).encode() + b"\0")
         with open(f, "rb") as fh:
