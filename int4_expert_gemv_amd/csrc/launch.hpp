@@ -45,6 +45,9 @@ struct MoeDecodeArgs {
   int parts;           // blocks per unique expert
   int rounds;          // tiles per wave
   int max_blocks;      // pipelined kernels: grid size cap (0 = default)
+  uint32_t* hq;        // workspace: h as digit words [T*k][I/16][8] (single-token int4 kernels)
+  float* hqs;          // workspace: their factors [T*k][I/16]
+  int hq_ready;        // hq already holds the digits of h (written by the gate+up kernel)
 };
 
 // qgemv.hip
@@ -103,6 +106,8 @@ QM_DECL_MOE(moe_down_i8_r)
 // moe_decode.hip
 hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
+// true when launch_moe_gate_up with these arguments also writes the digits of h to a.hq
+bool moe_gate_up_writes_digits(int fmt, const MoeDecodeArgs& a);
 
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
 // (or row length, per-row scales) is a multiple of 64 with at most 96 groups

@@ -2,6 +2,7 @@
 // kernels themselves are in moe_decode_impl.hpp, instantiated per format and
 // activation type in moe_decode_*.hip).
 #include "launch.hpp"
+#include "moe_t1_q.hpp"
 
 namespace qm {
 
@@ -16,6 +17,10 @@ hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArg
 hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st) {
   if (fmt == 4) return grouped ? moe_down_i4_g(a, st) : moe_down_i4_r(a, st);
   return moe_down_i8_r(a, st);
+}
+
+bool moe_gate_up_writes_digits(int fmt, const MoeDecodeArgs& a) {
+  return fmt == 4 && a.hq != nullptr && q_gate_up_ok(a);
 }
 
 }  // namespace qm

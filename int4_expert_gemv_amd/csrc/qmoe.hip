@@ -151,7 +151,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t decode_workspace(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k;
-  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256);
+  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256) + align_up(P * I * 2, 256) + align_up(P * I / 4, 256);
 }
 
 ExpertArgs expert_args(const qm_experts* ex) {
@@ -174,7 +174,8 @@ ExpertArgs expert_args(const qm_experts* ex) {
   return e;
 }
 
-// Decode workspace: h [T*k][I] fp32, then per-pair down outputs [T*k][H] fp32.
+// Decode workspace: h [T*k][I] fp32, per-pair down outputs [T*k][H] fp32, h as
+// digit words [T*k][I/16][8] u32 and their factors [T*k][I/16] fp32.
 MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32_t* ids, const float* w, int k,
                           float* y, void* workspace) {
   MoeDecodeArgs a{};
@@ -184,7 +185,12 @@ MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32
   a.w = w;
   char* ws = static_cast<char*>(workspace);
   a.h = reinterpret_cast<float*>(ws);
-  a.pout = reinterpret_cast<float*>(ws + align_up((size_t)T * k * e.I * 4, 256));
+  if (ws) {
+    const size_t P = (size_t)T * k;
+    a.pout = reinterpret_cast<float*>(ws + align_up(P * e.I * 4, 256));
+    a.hq = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.pout) + align_up(P * e.H * 4, 256));
+    a.hqs = reinterpret_cast<float*>(reinterpret_cast<char*>(a.hq) + align_up(P * e.I * 2, 256));
+  }
   a.y = y;
   a.T = T;
   a.topk = k;
@@ -313,6 +319,7 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
       MoeDecodeArgs a = decode_args(e, static_cast<const char*>(x) + (size_t)t0 * xs, nt,
                                     topk_ids + (size_t)t0 * top_k, topk_w + (size_t)t0 * top_k, top_k,
                                     y + (size_t)t0 * ex->hidden, workspace);
+      a.hq_ready = moe_gate_up_writes_digits(ex->fmt, a) ? 1 : 0;
       err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
       if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
     }
