@@ -25,8 +25,10 @@
 // an LDS ring (global_load_lds DMA, as in moe_t1_lds.hpp).  The block's h
 // values are kept in LDS and turned into digits in its epilogue, so the down
 // kernel reads them ready-made.  down: one wave per routed pair, the pair's
-// digits in registers, rows of the down matrix through an LDS ring, lane
-// partials combined in a fixed order as in the register-h kernel.
+// digits in registers, rows of the down matrix loaded straight into registers
+// (all of a wave's rows in flight at once; an LDS-ring variant takes the
+// shapes whose rows do not fit), lane partials combined in a fixed order as
+// in the register-h kernel.
 #pragma once
 #include "moe_t1_lds.hpp"
 
@@ -394,6 +396,85 @@ __global__ __launch_bounds__(kDT) void moe_down_t1q_kernel(MoeDecodeArgs a) {
   }
 }
 
+// ---- down + weighted combine, weights prefetched into registers ----------------
+// The same work split as moe_down_t1q_kernel, but a lane's share of one unit
+// (CPL 16-byte chunks and their scales) is small enough that a wave issues
+// the loads of all its NU units at once into registers: no LDS ring, every
+// byte of the wave's rows in flight from the start.  Units past the wave's
+// last row reload that row and are dropped.
+template <int L, int CPL, int NU, bool GROUPED>
+__global__ __launch_bounds__(kDT) void moe_down_t1qr_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_e[kTopkMax], s_p[kTopkMax], s_n;
+  __shared__ float s_w[kTopkMax];
+  constexpr int PPW = 64 / L;
+  const ExpertArgs& ex = a.ex;
+  routed_pairs(a.ids, a.w, a.topk, ex.E, s_e, s_p, s_w, &s_n);
+  __syncthreads();
+  const int np = s_n;
+  const int npg = (np + PPW - 1) / PPW;
+  int npg2 = 1;
+  while (npg2 < npg) npg2 <<= 1;
+  const int S = kDW / npg2;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int pg = wave % npg2, sl = wave / npg2;
+  const int qi = lane / L, sub = lane - qi * L;
+  const int q = pg * PPW + qi;
+  const bool qok = pg < npg && q < np;
+  const int qq = qok ? q : 0;
+  const int e = s_e[qq], prow = s_p[qq];
+  const float wq = qok ? s_w[qq] : 0.f;
+  const int R = (ex.H + gridDim.x - 1) / gridDim.x;
+  const int r0 = blockIdx.x * R, r1 = min(ex.H, r0 + R);
+  float* part = reinterpret_cast<float*>(lds);  // [R][kDW][64] lane partials
+  const int span = r1 - r0 - sl;
+  const int nunits = (pg < npg && span > 0) ? (span + S - 1) / S : 0;  // wave-uniform, <= NU
+  if (nunits > 0) {
+    u32x4 hd[CPL][4];
+    float hs[CPL][2];
+    const uint32_t* hqrow = a.hq + (int64_t)prow * (ex.I / 16) * 8;
+    const float* hsrow = a.hqs + (int64_t)prow * (ex.I / 16);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = sub + L * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hd[i][j] = *reinterpret_cast<const u32x4*>(hqrow + (size_t)c * 16 + j * 4);
+      hs[i][0] = hsrow[2 * c];
+      hs[i][1] = hsrow[2 * c + 1];
+    }
+    u32x4 wv[NU][CPL];
+    float sv[NU][CPL];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int r = r0 + sl + S * min(u, nunits - 1);
+      const int64_t er = (int64_t)e * ex.H + r;
+      const uint8_t* qrow = ex.dq + er * ex.rb_i;
+      const float* srow = ex.ds + er * ex.G_i;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = sub + L * i;
+        wv[u][i] = ld_stream(qrow + (int64_t)c * 16);
+        sv[u][i] = ld_stream(srow + (GROUPED ? (c >> ex.gshift) : 0));
+      }
+    }
+    const float wz = qok ? wq : 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) t = q_chunk(wv[u][i], hd[i], hs[i], sv[u][i], t);
+      if (u < nunits) part[((sl + S * u) * kDW + pg) * 64 + lane] = wz * t;
+    }
+  }
+  __syncthreads();
+  for (int i = wave; i < r1 - r0; i += kDW) {
+    float v = 0.f;
+    for (int g = 0; g < npg; ++g) v += part[(i * kDW + g) * 64 + lane];
+    v = group_sum<64>(v);
+    if (lane == 0) a.y[r0 + i] = v;
+  }
+}
+
 // ---- launch ---------------------------------------------------------------------
 
 #ifndef QM_T1Q
@@ -485,8 +566,38 @@ inline hipError_t try_gate_up_t1q(const MoeDecodeArgs& a, hipStream_t st) {
   }
 }
 
+#ifndef QM_T1QR
+#define QM_T1QR 1
+#endif
+#ifndef QM_T1QR_NU
+#define QM_T1QR_NU 8
+#endif
+
+// register-prefetch down kernel: units per wave = rows per block / row slices
+template <int L, int CPL, bool GROUPED>
+inline hipError_t launch_dn_t1qr(const MoeDecodeArgs& a, hipStream_t st) {
+  constexpr int NU = QM_T1QR_NU / CPL;
+  constexpr int PPW = 64 / L;
+  const int npg = (a.topk + PPW - 1) / PPW;
+  int npg2 = 1;
+  while (npg2 < npg) npg2 <<= 1;
+  if (!QM_T1QR || npg2 > kDW) return hipErrorNotSupported;
+  const int S = kDW / npg2;
+  const int blocks = (a.ex.H + NU * S - 1) / (NU * S);  // R = ceil(H / blocks) <= NU * S rows
+  const int R = (a.ex.H + blocks - 1) / blocks;
+  if ((R + S - 1) / S > NU) return hipErrorNotSupported;
+  const size_t lds = (size_t)R * kDW * 64 * 4;
+  if (lds > (size_t)kLdsMax) return hipErrorNotSupported;
+  hipLaunchKernelGGL((moe_down_t1qr_kernel<L, CPL, NU, GROUPED>), dim3(blocks), dim3(kDT), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int L, int CPL, bool GROUPED>
 inline hipError_t launch_dn_t1q(const MoeDecodeArgs& a, hipStream_t st) {
+  {
+    const hipError_t er = launch_dn_t1qr<L, CPL, GROUPED>(a, st);
+    if (er != hipErrorNotSupported) return er;
+  }
   constexpr int D = (CPL == 1 || L == 32) ? QM_T1Q_DN_D : (QM_T1Q_DN_D + 1) / 2;
   constexpr int PPW = 64 / L;
   const int npg = (a.topk + PPW - 1) / PPW;
