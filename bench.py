@@ -33,8 +33,8 @@ METRIC = "achieved HBM GB/s + µs/layer for int4-g64 MoE expert FFN decode (B=1)
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--config", default="moe_large", choices=["moe_large", "moe_35b", "moe_prefill", "gemv", "qprep", "copy"],
                    help="copy: a plain 1 GiB device-to-device copy, the reference kernel for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters")

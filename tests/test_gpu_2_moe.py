@@ -110,3 +110,54 @@ def test_moe_deterministic(q):
     y1 = run_moe(q, ex, d, x, ids, w)
     y2 = run_moe(q, ex, d, x, ids, w)
     assert np.array_equal(y1, y2)
+
+
+def _wide_range_x(seed, T, H, xdt):
+    """Activations spanning six decades, with all-zero 16-value groups and
+    groups holding one large value among tiny ones: the single-token kernels
+    scale every group of 16 activations by its own power of two, and this
+    case exercises that per-group exponent (and its zero case)."""
+    g = np.random.default_rng([seed, 12])
+    x = synth.normal_f32(g, (T, H)) * (10.0 ** g.uniform(-3, 3, size=(T, H))).astype(np.float32)
+    xg = x.reshape(T, H // 16, 16)
+    xg[:, ::7, :] = 0.0                          # whole groups of zeros
+    xg[:, 3::11, :] *= 1e-4                      # tiny groups ...
+    xg[:, 3::11, 5] = 40.0                       # ... with one large value
+    x = xg.reshape(T, H).astype(np.float32)
+    return synth.to_bf16_bits(x) if xdt == "bf16" else x
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_moe_one_token_wide_activation_range(q, oracle, xdt):
+    """hidden 6144, inter 2048, top-8, one token (the single-token kernels):
+    within the bar for activations of very different magnitudes."""
+    E, H, I, T, k = 24, 6144, 2048, 1, 8
+    ids, w = _routing(13, T, E, k)
+    ex = synth.expert_set(13, 4, E, H, I, 64, experts=np.unique(ids))
+    d = upload_experts(ex, only=np.unique(ids))
+    x = _wide_range_x(13, T, H, xdt)
+    y = run_moe(q, ex, d, x, ids, w)
+    yr, _, nr = oracle.moe_ffn(ex, x, ids, w)
+    assert norm_err(y, yr, nr) <= TOL
+
+
+def test_moe_one_token_stages_match_layer(q):
+    """moe_gate_up then moe_down (hidden vectors through the caller's buffer,
+    turned into digits by their own kernel) give the same y, bit for bit, as
+    moe_expert_ffn (digits written by the gate+up kernel itself)."""
+    E, H, I, T, k = 24, 6144, 2048, 1, 8
+    ids, w = _routing(14, T, E, k)
+    ex = synth.expert_set(14, 4, E, H, I, 64, experts=np.unique(ids))
+    d = upload_experts(ex, only=np.unique(ids))
+    x = synth.activations(np.random.default_rng(15), (T, H), "bf16")
+    e = q.experts(4, 64, d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
+    ws = torch.empty(q.moe_expert_ffn_workspace(e, T, k), dtype=torch.uint8, device="cuda")
+    y1 = torch.full((T, H), float("nan"), device="cuda")
+    y2 = torch.full((T, H), float("nan"), device="cuda")
+    h = torch.empty((T * k, I), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(w)
+    q.moe_expert_ffn(e, xd, idd, wd, y1, ws)
+    q.moe_gate_up(e, xd, idd, h)
+    q.moe_down(e, h, idd, wd, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
