@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--graph", action="store_true",
+                   help="gemv / qprep: time the calls as one HIP graph replay (no per-call host launch cost) "
+                        "instead of back-to-back launches from Python")
     return p.parse_args()
 
 
@@ -316,6 +319,30 @@ def bench_prefill(args):
             "cpu_baseline": None}
 
 
+def graph_ms(fn, steps):
+    """ms per call of fn(0..steps-1) captured into one HIP graph and replayed
+    (events on the replay stream around the second replay)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for j in range(steps):
+            fn(j)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def bench_gemv(args):
     import torch
     from int4_expert_gemv_amd import qmoe, synth
@@ -362,6 +389,8 @@ def bench_gemv(args):
             fn(i % copies)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.graph:
+            return graph_ms(lambda j: fn(j % copies), args.steps)
         start.record()
         for j in range(args.steps):
             fn(j % copies)
@@ -388,7 +417,8 @@ def bench_gemv(args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": ("qgemv_pair %dx%d + %dx%d" % (n, k, n2, k) if n2 else
                                     "%s %dx%d" % ("qgemv" if B == 1 else "qgemm_small", n, k)) +
-                                   " %s, bf16 x, batch %d, %d weight copies in rotation" % (wname, B, copies)},
+                                   " %s, bf16 x, batch %d, %d weight copies in rotation" % (wname, B, copies),
+                       "timing": "HIP graph replay" if args.graph else "back-to-back launches from Python"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,
@@ -437,6 +467,8 @@ def bench_qprep(args):
             fn(i % copies)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.graph:
+            return graph_ms(lambda j: fn(j % copies), args.steps)
         start.record()
         for j in range(args.steps):
             fn(j % copies)
@@ -444,7 +476,9 @@ def bench_qprep(args):
         torch.cuda.synchronize()
         return start.elapsed_time(end) / args.steps
 
-    host_ms = timed(host_norm)
+    g_flag, args.graph = args.graph, False
+    host_ms = timed(host_norm)  # synchronises with the host on every call: never captured
+    args.graph = g_flag
     ms = timed(chain)
     o = ref.oracle()
     ur, _ = o.gemv(*mats[0][0], x_h)
@@ -459,7 +493,8 @@ def bench_qprep(args):
             "us_per_call": round(ms * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": "qgemv_norm_chain: %d -> (%d, %d), rmsnorm, %d -> %d, int4-g64, bf16 x, "
-                                   "%d weight sets in rotation" % (k, na, nkv, na, nq, copies)},
+                                   "%d weight sets in rotation" % (k, na, nkv, na, nq, copies),
+                       "timing": "HIP graph replay" if args.graph else "back-to-back launches from Python"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,

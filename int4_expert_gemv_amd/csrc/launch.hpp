@@ -50,6 +50,10 @@ struct MoeDecodeArgs {
   int hq_ready;        // hq already holds the digits of h (written by the gate+up kernel)
 };
 
+// qgemv_q.hip: single-token int4 GEMV on integer dot products (k = 2048 *
+// {1,2,3,4,6,8}); hipErrorNotSupported for other calls
+hipError_t launch_qgemv_q(int xdt, bool grouped, const GemvArgs& a, hipStream_t st);
+hipError_t launch_qgemv_q_pair(int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st);
 // qgemv.hip
 int lanes_per_row(int kchunks);
 int rows_per_unit(int L, int NB);

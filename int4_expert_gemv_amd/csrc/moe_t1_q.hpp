@@ -83,6 +83,16 @@ __device__ __forceinline__ float q_group16(const float (&v)[16], uint32_t (&wd)[
   return ldexpf(1.f, E - 15);
 }
 
+// Workgroup barrier for LDS only: waits for this wave's LDS operations, not
+// for its outstanding global loads (__syncthreads() would also wait for
+// every load in flight, here the weight prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
 }

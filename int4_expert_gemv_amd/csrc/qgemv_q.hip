@@ -1,0 +1,197 @@
+// qgemv_q.hip -- single-token int4 GEMV on integer dot products: y = W x for
+// one resident quantized tensor, the dense quantized GEMV of the colibri page
+// "Vulkan backend: expert tier + dense + MLA attention on any Vulkan 1.2 GPU"
+// (commit notes "backend_vulkan.c/.h + shaders/qmatmul.comp" and "fmt=4
+// grouped scales"), with x turned into the digit words of moe_t1_q.hpp so
+// that one v_dot8_i32_i4 handles eight weights.
+//
+// Two matrices of the same x (and k, format, grouping) can share one launch:
+// workgroups [0, nba) work on the first, the rest on the second.
+//
+// Work split: workgroups of eight waves; wave w of workgroup b owns NU
+// consecutive rows and a lane owns chunks lane + 64 cb (cb < CB, K = 2048 CB)
+// of each of them.  A lane's share of a row is CB 16-byte chunks and their
+// scales, so the wave issues the loads of all NU rows at once into registers
+// (no staging: every byte of the call is in flight from the start, the grid
+// is sized to one workgroup per CU).  x is fetched first (loads complete in
+// order), turned into digits once per workgroup in LDS while the weights
+// stream in, and read back per row (or kept in registers for short rows).
+#include <type_traits>
+
+#include "moe_t1_q.hpp"
+
+namespace qm {
+
+constexpr int kQvWaves = 8;
+constexpr int kQvThreads = 64 * kQvWaves;
+
+template <int XT, int CB, int NU, bool GROUPED>
+__global__ __launch_bounds__(kQvThreads) void qgemv_q_kernel(GemvArgs a0, GemvArgs b0, int nba) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int K = 2048 * CB;
+  constexpr bool XREG = CB <= 4;  // keep the lane's x digits in registers
+  const bool first = (int)blockIdx.x < nba;
+  const GemvArgs& a = first ? a0 : b0;
+  const int blk = first ? (int)blockIdx.x : (int)blockIdx.x - nba;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rb = (blk * kQvWaves + wave) * NU;  // this wave's first row
+  uint32_t* xq = reinterpret_cast<uint32_t*>(lds);          // [K/16][8]
+  float* xsc = reinterpret_cast<float*>(lds + (size_t)K * 2);  // [K/16]
+
+  // x first
+  constexpr int NG = (K / 16 + kQvThreads - 1) / kQvThreads;
+  constexpr int NR = XT == kBF16 ? 2 : 4;
+  u32x4 raw[NG][NR];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = threadIdx.x + gi * kQvThreads;
+    if (g < K / 16) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + (size_t)g * 16 * (XT == kBF16 ? 2 : 4));
+#pragma unroll
+      for (int r = 0; r < NR; ++r) raw[gi][r] = src[r];
+    }
+  }
+  // then every row of this wave
+  u32x4 wv[NU][CB];
+  float sv[NU][CB];
+  const bool won = rb < a.n;
+  if (won) {  // chunk-major, the order the arithmetic consumes them
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int r = min(rb + u, a.n - 1);
+        wv[u][cb] = ld_stream(a.q + (int64_t)r * a.row_bytes + (int64_t)c * 16);
+        sv[u][cb] = ld_stream(a.s + (int64_t)r * a.G + (GROUPED ? (c >> a.gshift) : 0));
+      }
+    }
+  }
+  // x digits, once per workgroup
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = threadIdx.x + gi * kQvThreads;
+    if (g < K / 16) {
+      float v[16];
+      if constexpr (XT == kBF16) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * r + 2 * i] = __uint_as_float(raw[gi][r][i] << 16);
+            v[8 * r + 2 * i + 1] = __uint_as_float(raw[gi][r][i] & 0xFFFF0000u);
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * r + i] = __uint_as_float(raw[gi][r][i]);
+      }
+      uint32_t wd[8];
+      xsc[g] = q_group16(v, wd);
+      u32x4* dst = reinterpret_cast<u32x4*>(xq + (size_t)g * 8);
+      dst[0] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      dst[1] = u32x4{wd[4], wd[5], wd[6], wd[7]};
+    }
+  }
+  lds_barrier();
+  if (!won) return;
+  u32x4 xr[XREG ? CB : 1][4];
+  float xsr[XREG ? CB : 1][2];
+  if constexpr (XREG) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xq + (size_t)c * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[cb][j] = src[j];
+      xsr[cb][0] = xsc[2 * c];
+      xsr[cb][1] = xsc[2 * c + 1];
+    }
+  }
+  // a chunk's x digits are read once for all NU rows
+  float acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if constexpr (XREG) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] = q_chunk(wv[u][cb], xr[cb], xsr[cb], sv[u][cb], acc[u]);
+    } else {
+      const int c = lane + 64 * cb;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xq + (size_t)c * 16);
+      const u32x4 xd[4] = {src[0], src[1], src[2], src[3]};
+      const float xs[2] = {xsc[2 * c], xsc[2 * c + 1]};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] = q_chunk(wv[u][cb], xd, xs, sv[u][cb], acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const float yv = group_sum<64>(acc[u]);
+    if (lane == 0 && rb + u < a.n) a.y[rb + u] = yv;
+  }
+}
+
+// rows per wave: enough that one workgroup per CU covers n, within the
+// register budget of CB * NU 16-byte chunks per lane
+template <int XT, int CB, bool GROUPED>
+hipError_t launch_qv(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_t st) {
+  constexpr int kCus = 256;
+  const int rows_all = a.n + (pair ? b.n : 0);
+  const int need = (rows_all + kCus * kQvWaves - 1) / (kCus * kQvWaves);
+  constexpr int cap = CB <= 3 ? 8 : (CB <= 4 ? 6 : 4);
+  const size_t lds = (size_t)2048 * CB * 2 + (size_t)2048 * CB / 4;
+  auto go = [&](auto nu_tag) {
+    constexpr int NU = decltype(nu_tag)::value;
+    const int rows = kQvWaves * NU;
+    const int nba = (a.n + rows - 1) / rows;
+    const int nbb = pair ? (b.n + rows - 1) / rows : 0;
+    hipLaunchKernelGGL((qgemv_q_kernel<XT, CB, NU, GROUPED>), dim3(nba + nbb), dim3(kQvThreads), lds, st, a,
+                       pair ? b : a, nba);
+    return hipGetLastError();
+  };
+  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 2) return go(std::integral_constant<int, 2>{});
+  if (need <= 3 || cap <= 3) return go(std::integral_constant<int, (cap < 3 ? cap : 3)>{});
+  if (need <= 4 || cap <= 4) return go(std::integral_constant<int, 4>{});
+  if (need <= 6 || cap <= 6) return go(std::integral_constant<int, (cap < 6 ? cap : 6)>{});
+  return go(std::integral_constant<int, cap>{});
+}
+
+template <int XT, bool GROUPED>
+hipError_t launch_qv_cb(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_t st) {
+  switch (a.k / 2048) {
+    case 1: return launch_qv<XT, 1, GROUPED>(a, b, pair, st);
+    case 2: return launch_qv<XT, 2, GROUPED>(a, b, pair, st);
+    case 3: return launch_qv<XT, 3, GROUPED>(a, b, pair, st);
+    case 4: return launch_qv<XT, 4, GROUPED>(a, b, pair, st);
+    case 6: return launch_qv<XT, 6, GROUPED>(a, b, pair, st);
+    case 8: return launch_qv<XT, 8, GROUPED>(a, b, pair, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+#ifndef QM_QGEMV_Q
+#define QM_QGEMV_Q 1
+#endif
+
+// int4 (grouped or per row), one token, k = 2048 * {1,2,3,4,6,8}, x 16-byte
+// aligned; hipErrorNotSupported otherwise (the caller runs the other kernels)
+hipError_t launch_qgemv_q(int xdt, bool grouped, const GemvArgs& a, hipStream_t st) {
+  if (!QM_QGEMV_Q || a.n < 1 || a.k % 2048 || ((uintptr_t)a.x & 15) != 0) return hipErrorNotSupported;
+  if (xdt == kBF16) return grouped ? launch_qv_cb<kBF16, true>(a, a, false, st) : launch_qv_cb<kBF16, false>(a, a, false, st);
+  return grouped ? launch_qv_cb<kF32, true>(a, a, false, st) : launch_qv_cb<kF32, false>(a, a, false, st);
+}
+
+// two int4 matrices of one x in one launch (same k and grouping)
+hipError_t launch_qgemv_q_pair(int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st) {
+  if (!QM_QGEMV_Q || a.n < 1 || b.n < 1 || a.k != b.k || a.k % 2048 || ((uintptr_t)a.x & 15) != 0)
+    return hipErrorNotSupported;
+  if (xdt == kBF16) return grouped ? launch_qv_cb<kBF16, true>(a, b, true, st) : launch_qv_cb<kBF16, false>(a, b, true, st);
+  return grouped ? launch_qv_cb<kF32, true>(a, b, true, st) : launch_qv_cb<kF32, false>(a, b, true, st);
+}
+
+}  // namespace qm
