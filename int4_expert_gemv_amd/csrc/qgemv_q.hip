@@ -135,6 +135,184 @@ __global__ __launch_bounds__(kQvThreads) void qgemv_q_kernel(GemvArgs a0, GemvAr
   }
 }
 
+// ---- int8 per-row weights ------------------------------------------------------
+// The same scheme with v_dot4_i32_i8: the integers X of a group of 16
+// activations (as above, |X| <= 30567) are written with two balanced base-256
+// digits, byte pattern X & 255 and ((X + 128) >> 8) & 255 (range [-32896,
+// 32639]); digit d of activations 4j..4j+3 is word j*2+d.  A 16-byte chunk
+// holds 16 int8 weights = one group: eight dot4 give its two digit sums,
+// recombined as a0 + 256 a1 (exact in int32), scaled by 2^(E-15); the row's
+// scale multiplies the row sum.
+__device__ __forceinline__ float q8_group16(const float (&v)[16], uint32_t (&wd)[8]) {
+  const int E = q_exp(q_amax16(v));
+  int X[16];
+  q_ints16(v, E, X);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0 |= ((uint32_t)X[4 * j + i] & 255u) << (8 * i);
+      w1 |= ((uint32_t)((X[4 * j + i] + 128) >> 8) & 255u) << (8 * i);
+    }
+    wd[j * 2] = w0;
+    wd[j * 2 + 1] = w1;
+  }
+  return ldexpf(1.f, E - 15);
+}
+
+__device__ __forceinline__ float q8_chunk(const u32x4& w, const u32x4 (&xd)[2], float xs, float acc) {
+  int a0 = 0, a1 = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = xd[j >> 1][(j & 1) * 2], hi = xd[j >> 1][(j & 1) * 2 + 1];
+    a0 = __builtin_amdgcn_sdot4((int)w[j], (int)lo, a0, false);
+    a1 = __builtin_amdgcn_sdot4((int)w[j], (int)hi, a1, false);
+  }
+  const int t = (int)((uint32_t)a0 + ((uint32_t)a1 << 8));
+  return __builtin_fmaf((float)t, xs, acc);
+}
+
+// K = 1024 CB int8 values per row (a lane owns chunks lane + 64 cb)
+template <int XT, int CB, int NU>
+__global__ __launch_bounds__(kQvThreads) void qgemv_q8_kernel(GemvArgs a0, GemvArgs b0, int nba) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int K = 1024 * CB;
+  constexpr bool XREG = CB <= 6;
+  const bool first = (int)blockIdx.x < nba;
+  const GemvArgs& a = first ? a0 : b0;
+  const int blk = first ? (int)blockIdx.x : (int)blockIdx.x - nba;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rb = (blk * kQvWaves + wave) * NU;
+  uint32_t* xq = reinterpret_cast<uint32_t*>(lds);             // [K/16][8]
+  float* xsc = reinterpret_cast<float*>(lds + (size_t)K * 2);  // [K/16]
+  constexpr int NG = (K / 16 + kQvThreads - 1) / kQvThreads;
+  constexpr int NR = XT == kBF16 ? 2 : 4;
+  u32x4 raw[NG][NR];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = threadIdx.x + gi * kQvThreads;
+    if (g < K / 16) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + (size_t)g * 16 * (XT == kBF16 ? 2 : 4));
+#pragma unroll
+      for (int r = 0; r < NR; ++r) raw[gi][r] = src[r];
+    }
+  }
+  u32x4 wv[NU][CB];
+  float sr[NU];
+  const bool won = rb < a.n;
+  if (won) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) sr[u] = a.s[min(rb + u, a.n - 1)];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        wv[u][cb] = ld_stream(a.q + (int64_t)min(rb + u, a.n - 1) * a.row_bytes + (int64_t)c * 16);
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = threadIdx.x + gi * kQvThreads;
+    if (g < K / 16) {
+      float v[16];
+      if constexpr (XT == kBF16) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * r + 2 * i] = __uint_as_float(raw[gi][r][i] << 16);
+            v[8 * r + 2 * i + 1] = __uint_as_float(raw[gi][r][i] & 0xFFFF0000u);
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * r + i] = __uint_as_float(raw[gi][r][i]);
+      }
+      uint32_t wd[8];
+      xsc[g] = q8_group16(v, wd);
+      u32x4* dst = reinterpret_cast<u32x4*>(xq + (size_t)g * 8);
+      dst[0] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      dst[1] = u32x4{wd[4], wd[5], wd[6], wd[7]};
+    }
+  }
+  lds_barrier();
+  if (!won) return;
+  u32x4 xr[XREG ? CB : 1][2];
+  float xsr[XREG ? CB : 1];
+  if constexpr (XREG) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xq + (size_t)c * 8);
+      xr[cb][0] = src[0];
+      xr[cb][1] = src[1];
+      xsr[cb] = xsc[c];
+    }
+  }
+  float acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if constexpr (XREG) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] = q8_chunk(wv[u][cb], xr[cb], xsr[cb], acc[u]);
+    } else {
+      const int c = lane + 64 * cb;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xq + (size_t)c * 8);
+      const u32x4 xd[2] = {src[0], src[1]};
+      const float xs = xsc[c];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] = q8_chunk(wv[u][cb], xd, xs, acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const float yv = group_sum<64>(acc[u]);
+    if (lane == 0 && rb + u < a.n) a.y[rb + u] = sr[u] * yv;
+  }
+}
+
+template <int XT, int CB>
+hipError_t launch_qv8(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_t st) {
+  constexpr int kCus = 256;
+  const int rows_all = a.n + (pair ? b.n : 0);
+  const int need = (rows_all + kCus * kQvWaves - 1) / (kCus * kQvWaves);
+  constexpr int cap = CB <= 4 ? 8 : (CB <= 8 ? 4 : 2);
+  const size_t lds = (size_t)1024 * CB * 2 + (size_t)1024 * CB / 4;
+  auto go = [&](auto nu_tag) {
+    constexpr int NU = decltype(nu_tag)::value;
+    const int rows = kQvWaves * NU;
+    const int nba = (a.n + rows - 1) / rows;
+    const int nbb = pair ? (b.n + rows - 1) / rows : 0;
+    hipLaunchKernelGGL((qgemv_q8_kernel<XT, CB, NU>), dim3(nba + nbb), dim3(kQvThreads), lds, st, a, pair ? b : a,
+                       nba);
+    return hipGetLastError();
+  };
+  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 2 || cap <= 2) return go(std::integral_constant<int, 2>{});
+  if (need <= 3) return go(std::integral_constant<int, 3>{});
+  if (need <= 4 || cap <= 4) return go(std::integral_constant<int, 4>{});
+  return go(std::integral_constant<int, cap>{});
+}
+
+template <int XT>
+hipError_t launch_qv8_cb(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_t st) {
+  switch (a.k / 1024) {
+    case 2: return launch_qv8<XT, 2>(a, b, pair, st);
+    case 4: return launch_qv8<XT, 4>(a, b, pair, st);
+    case 6: return launch_qv8<XT, 6>(a, b, pair, st);
+    case 8: return launch_qv8<XT, 8>(a, b, pair, st);
+    case 12: return launch_qv8<XT, 12>(a, b, pair, st);
+    case 16: return launch_qv8<XT, 16>(a, b, pair, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 // rows per wave: enough that one workgroup per CU covers n, within the
 // register budget of CB * NU 16-byte chunks per lane
 template <int XT, int CB, bool GROUPED>
@@ -184,6 +362,18 @@ hipError_t launch_qgemv_q(int xdt, bool grouped, const GemvArgs& a, hipStream_t 
   if (!QM_QGEMV_Q || a.n < 1 || a.k % 2048 || ((uintptr_t)a.x & 15) != 0) return hipErrorNotSupported;
   if (xdt == kBF16) return grouped ? launch_qv_cb<kBF16, true>(a, a, false, st) : launch_qv_cb<kBF16, false>(a, a, false, st);
   return grouped ? launch_qv_cb<kF32, true>(a, a, false, st) : launch_qv_cb<kF32, false>(a, a, false, st);
+}
+
+// int8 per row, one token, k = 1024 * {2,4,6,8,12,16}, x 16-byte aligned
+hipError_t launch_qgemv_q8(int xdt, const GemvArgs& a, hipStream_t st) {
+  if (!QM_QGEMV_Q || a.n < 1 || a.k % 1024 || ((uintptr_t)a.x & 15) != 0) return hipErrorNotSupported;
+  return xdt == kBF16 ? launch_qv8_cb<kBF16>(a, a, false, st) : launch_qv8_cb<kF32>(a, a, false, st);
+}
+
+hipError_t launch_qgemv_q8_pair(int xdt, const GemvArgs& a, const GemvArgs& b, hipStream_t st) {
+  if (!QM_QGEMV_Q || a.n < 1 || b.n < 1 || a.k != b.k || a.k % 1024 || ((uintptr_t)a.x & 15) != 0)
+    return hipErrorNotSupported;
+  return xdt == kBF16 ? launch_qv8_cb<kBF16>(a, b, true, st) : launch_qv8_cb<kF32>(a, b, true, st);
 }
 
 // two int4 matrices of one x in one launch (same k and grouping)

@@ -116,6 +116,10 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
                                          static_cast<hipStream_t>(stream));
     if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
   }
+  if (w->fmt == QM_FMT_INT8_ROW && batch == 1) {
+    const hipError_t eq = launch_qgemv_q8(xdt, a, static_cast<hipStream_t>(stream));
+    if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   const int NB = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
   hipError_t err = launch_qgemv(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, NB,
                                 static_cast<hipStream_t>(stream));
@@ -247,6 +251,12 @@ int qgemv_pair(const qm_qmat* w1, const qm_qmat* w2, const void* x, int32_t x_dt
   if (w1->fmt == QM_FMT_INT4 && w2->fmt == QM_FMT_INT4 && (g1 != 0) == (g2 != 0)) {
     const hipError_t eq = launch_qgemv_q_pair(x_dtype, g1 != 0, gemv_args(w1, x, 1, w1->k, y1, w1->n),
                                               gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
+    if (eq == hipSuccess) return QM_OK;
+    if (eq != hipErrorNotSupported) return QM_ERR_LAUNCH;
+  }
+  if (w1->fmt == QM_FMT_INT8_ROW && w2->fmt == QM_FMT_INT8_ROW) {
+    const hipError_t eq = launch_qgemv_q8_pair(x_dtype, gemv_args(w1, x, 1, w1->k, y1, w1->n),
+                                               gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
     if (eq == hipSuccess) return QM_OK;
     if (eq != hipErrorNotSupported) return QM_ERR_LAUNCH;
   }
