@@ -49,6 +49,13 @@
  *    group_size must be 64.  qgemv, qgemv_pair and qgemm_small with batch 1
  *    take it (k <= 16384); the expert FFN does not (QM_ERR_UNSUPPORTED).
  *  Value = element * its scale.  Accumulation on the GPU is fp32.
+ *  Single-token int4 and int8 calls (qgemv, qgemv_pair, the one-token
+ *  expert FFN: the shapes listed with each entry point's fast path) take
+ *  integer dot products: each group of 16 consecutive activations (x, and the
+ *  expert FFN's hidden vector) is scaled by a power of two and rounded to
+ *  integers of at most 15 bits, so an activation is off by at most
+ *  2^-15 * 1.072 * (largest |activation| of its group); small-integer
+ *  activations are exact.  Non-finite activations are not supported there.
  *
  * Shape limits of the GPU path (QM_ERR_UNSUPPORTED otherwise): int4 needs
  * k % 32 == 0, int8 needs k % 16 == 0; 1 <= k <= QM_K_MAX; q and x must be
@@ -113,7 +120,9 @@ typedef struct {
 
 /* y[r] = sum_c W[r][c] * x[c], r < w->n.
  * [V: qmatmul.comp note -- the dense quantized GEMV, one token]
- * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).       */
+ * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).
+ * Fast path (integer dot products): int4 with k a multiple of 2048 up to
+ * 16384, int8 per row with k a multiple of 1024 up to 16384.               */
 QM_API int qgemv(const qm_qmat *w, const void *x, int32_t x_dtype, float *y, void *stream);
 
 /* Two projections of one x: y1 = W1 x and y2 = W2 x (W1, W2 with the same k).

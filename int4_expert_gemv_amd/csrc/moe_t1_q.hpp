@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
       dst[1] = u32x4{wd[4], wd[5], wd[6], wd[7]};
     }
   }
-  __syncthreads();
+  lds_barrier();  // the digits are in LDS; the weight DMA stays in flight
   u32x4 xd[CB][4];
   float xs[CB][2];
 #pragma unroll
