@@ -1,5 +1,5 @@
-// moe_t1_q.hpp -- single-token routed expert FFN (int4 experts) on integer
-// dot products: the K-expert group of the colibri page "Vulkan backend:
+// moe_t1_q.hpp -- routed expert FFN decode (int4 experts, 1..8 tokens, every
+// routed (token, slot) pair on its own) on integer dot products: the K-expert group of the colibri page "Vulkan backend:
 // expert tier + dense + MLA attention on any Vulkan 1.2 GPU" (gate+up with
 // SiLU, then the down projection combined with the routing weights), with the
 // activations turned into small integers so that one v_dot8_i32_i4 handles
@@ -20,11 +20,14 @@
 // accumulation is X_i itself: at most 2^-15 * 1.072 * max|v| per activation
 // of the group (exact for activations that are small integers).
 //
-// gate+up: one workgroup per (routed pair, tile of RPB rows of the
-// intermediate dimension); each wave streams its rows of gate and up through
+// gate+up: one workgroup per (routed pair p = token * top_k + slot, tile of
+// RPB rows of the intermediate dimension); each wave streams its rows of gate and up through
 // an LDS ring (global_load_lds DMA, as in moe_t1_lds.hpp).  The block's h
 // values are kept in LDS and turned into digits in its epilogue, so the down
-// kernel reads them ready-made.  down: one wave per routed pair, the pair's
+// kernel reads them ready-made.  Several tokens are served pair by pair: an
+// expert routed by two tokens is read twice (with independent routing over
+// hundreds of experts that is rare).  down: one row of workgroups per token,
+// one wave per routed pair of that token, the pair's
 // digits in registers, rows of the down matrix loaded straight into registers
 // (all of a wave's rows in flight at once; an LDS-ring variant takes the
 // shapes whose rows do not fit), lane partials combined in a fixed order as
@@ -144,9 +147,10 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
   static_assert(RPB % 16 == 0 && RPB % kWaves == 0, "tile of whole digit groups");
   const ExpertArgs& ex = a.ex;
   const int ntile = ex.I / RPB;
-  const int p = blockIdx.x / ntile, r0 = (blockIdx.x - p * ntile) * RPB;
+  const int p = blockIdx.x / ntile, r0 = (blockIdx.x - p * ntile) * RPB;  // pair p = token * topk + slot
   const int id = a.ids[p];
   if (id < 0 || id >= ex.E) return;  // the down kernel skips this slot
+  const char* xt = static_cast<const char*>(a.x) + (size_t)(p / a.topk) * ex.H * (XT == kBF16 ? 2 : 4);
   const int e = uniform(id);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = ex.H;
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
   for (int gi = 0; gi < NG; ++gi) {
     const int g = threadIdx.x + gi * kThreads;
     if (g < H / 16) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + (size_t)g * 16 * (XT == kBF16 ? 2 : 4));
+      const u32x4* src = reinterpret_cast<const u32x4*>(xt + (size_t)g * 16 * (XT == kBF16 ? 2 : 4));
 #pragma unroll
       for (int r = 0; r < NR; ++r) raw[gi][r] = src[r];
     }
@@ -419,7 +423,8 @@ __global__ __launch_bounds__(kDT) void moe_down_t1qr_kernel(MoeDecodeArgs a) {
   __shared__ float s_w[kTopkMax];
   constexpr int PPW = 64 / L;
   const ExpertArgs& ex = a.ex;
-  routed_pairs(a.ids, a.w, a.topk, ex.E, s_e, s_p, s_w, &s_n);
+  const int tok = blockIdx.y;  // token; its routed pairs are rows tok * topk + slot of h
+  routed_pairs(a.ids + tok * a.topk, a.w + tok * a.topk, a.topk, ex.E, s_e, s_p, s_w, &s_n);
   __syncthreads();
   const int np = s_n;
   const int npg = (np + PPW - 1) / PPW;
@@ -432,10 +437,11 @@ __global__ __launch_bounds__(kDT) void moe_down_t1qr_kernel(MoeDecodeArgs a) {
   const int q = pg * PPW + qi;
   const bool qok = pg < npg && q < np;
   const int qq = qok ? q : 0;
-  const int e = s_e[qq], prow = s_p[qq];
+  const int e = s_e[qq], prow = tok * a.topk + s_p[qq];
   const float wq = qok ? s_w[qq] : 0.f;
   const int R = (ex.H + gridDim.x - 1) / gridDim.x;
   const int r0 = blockIdx.x * R, r1 = min(ex.H, r0 + R);
+  float* yt = a.y + (int64_t)tok * ex.H;
   float* part = reinterpret_cast<float*>(lds);  // [R][kDW][64] lane partials
   const int span = r1 - r0 - sl;
   const int nunits = (pg < npg && span > 0) ? (span + S - 1) / S : 0;  // wave-uniform, <= NU
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(kDT) void moe_down_t1qr_kernel(MoeDecodeArgs a) {
     float v = 0.f;
     for (int g = 0; g < npg; ++g) v += part[(i * kDW + g) * 64 + lane];
     v = group_sum<64>(v);
-    if (lane == 0) a.y[r0 + i] = v;
+    if (lane == 0) yt[r0 + i] = v;
   }
 }
 
@@ -490,6 +496,7 @@ __global__ __launch_bounds__(kDT) void moe_down_t1qr_kernel(MoeDecodeArgs a) {
 #ifndef QM_T1Q
 #define QM_T1Q 1
 #endif
+constexpr int kQMaxTokens = 8;  // tokens per decode pass (one workgroup row of the grid per token in down)
 #ifndef QM_T1Q_GU_MIN_CB
 #define QM_T1Q_GU_MIN_CB 1
 #endif
@@ -509,12 +516,12 @@ inline size_t q_gu_lds(int H) {
 }
 
 // rows per gate+up tile: 32 when that still gives two workgroups per CU
-inline int q_gu_rpb(const MoeDecodeArgs& a) { return (a.topk * (a.ex.I / 32) >= 512) ? 32 : 16; }
+inline int q_gu_rpb(const MoeDecodeArgs& a) { return (a.T * a.topk * (a.ex.I / 32) >= 512) ? 32 : 16; }
 
 // Does the digit gate+up kernel take this call?  int4 experts, one token,
 // H = 2048 * CB (CB <= 4), I a multiple of 32 and of the row tile.
 inline bool q_gate_up_ok(const MoeDecodeArgs& a) {
-  if (!QM_T1Q || a.T != 1 || a.topk > kTopkMax) return false;
+  if (!QM_T1Q || a.T < 1 || a.T > kQMaxTokens || a.topk > kTopkMax) return false;
   if (a.ex.H % 2048 || a.ex.H / 2048 > 4 || a.ex.H / 2048 < QM_T1Q_GU_MIN_CB) return false;
   if (a.ex.I % 32 || a.ex.I % q_gu_rpb(a)) return false;
   if (((uintptr_t)a.x & 15) != 0) return false;
@@ -525,7 +532,7 @@ inline bool q_gate_up_ok(const MoeDecodeArgs& a) {
 // down row of 64 or 128 chunks (L = 64) or, for 9..16 slots, of 64 chunks
 // with two pairs per wave; needs the digit buffers.
 inline bool q_down_shape(const MoeDecodeArgs& a, int* L, int* cpl) {
-  if (!QM_T1Q || a.T != 1 || a.topk > kTopkMax || !a.hq) return false;
+  if (!QM_T1Q || a.T < 1 || a.T > kQMaxTokens || a.topk > kTopkMax || !a.hq) return false;
   const int kch = a.ex.I / 32;
   if (a.ex.I % 32) return false;
   if (kch % 64 == 0 && kch / 64 <= 2 && a.topk <= kDW) {
@@ -546,7 +553,7 @@ inline hipError_t launch_gu_t1q(const MoeDecodeArgs& a, hipStream_t st) {
   const size_t lds = q_gu_lds<CB, PS>(a.ex.H);
   if (lds > (size_t)kLdsMax) return hipErrorNotSupported;
   const int rpb = q_gu_rpb(a);
-  const int blocks = a.topk * (a.ex.I / rpb);
+  const int blocks = a.T * a.topk * (a.ex.I / rpb);
   if (rpb == 32)
     hipLaunchKernelGGL((moe_gate_up_t1q_kernel<XT, CB, 32, D, GROUPED, PS>), dim3(blocks), dim3(kThreads), lds, st,
                        a);
@@ -598,7 +605,7 @@ inline hipError_t launch_dn_t1qr(const MoeDecodeArgs& a, hipStream_t st) {
   if ((R + S - 1) / S > NU) return hipErrorNotSupported;
   const size_t lds = (size_t)R * kDW * 64 * 4;
   if (lds > (size_t)kLdsMax) return hipErrorNotSupported;
-  hipLaunchKernelGGL((moe_down_t1qr_kernel<L, CPL, NU, GROUPED>), dim3(blocks), dim3(kDT), lds, st, a);
+  hipLaunchKernelGGL((moe_down_t1qr_kernel<L, CPL, NU, GROUPED>), dim3(blocks, a.T), dim3(kDT), lds, st, a);
   return hipGetLastError();
 }
 
@@ -606,7 +613,7 @@ template <int L, int CPL, bool GROUPED>
 inline hipError_t launch_dn_t1q(const MoeDecodeArgs& a, hipStream_t st) {
   {
     const hipError_t er = launch_dn_t1qr<L, CPL, GROUPED>(a, st);
-    if (er != hipErrorNotSupported) return er;
+    if (er != hipErrorNotSupported || a.T != 1) return er;  // the ring kernel below takes one token
   }
   constexpr int D = (CPL == 1 || L == 32) ? QM_T1Q_DN_D : (QM_T1Q_DN_D + 1) / 2;
   constexpr int PPW = 64 / L;
@@ -631,7 +638,7 @@ inline hipError_t try_down_t1q(const MoeDecodeArgs& a, bool hq_ready, hipStream_
   int L = 0, cpl = 0;
   if (!q_down_shape(a, &L, &cpl)) return hipErrorNotSupported;
   if (!hq_ready) {
-    const int ngroups = a.topk * (a.ex.I / 16);
+    const int ngroups = a.T * a.topk * (a.ex.I / 16);
     hipLaunchKernelGGL(hq_digits_kernel<256>, dim3((ngroups + 255) / 256), dim3(256), 0, st, a.h, a.hq, a.hqs, ngroups);
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;

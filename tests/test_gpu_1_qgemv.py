@@ -131,3 +131,33 @@ def test_rejected_call_leaves_output(q):
         q.qgemv(m, dev(np.zeros(544, np.uint16)), y)
     torch.cuda.synchronize()
     assert torch.all(y == 3.0)
+
+
+def _wide_range_x(seed, k, xdt):
+    """Activations spanning six decades, with all-zero groups of 16 and groups
+    holding one large value among tiny ones (the single-token fast paths give
+    each group of 16 activations its own power-of-two scale)."""
+    g = np.random.default_rng([seed, 21])
+    x = synth.normal_f32(g, (k,)) * (10.0 ** g.uniform(-3, 3, size=k)).astype(np.float32)
+    xg = x.reshape(k // 16, 16)
+    xg[::5] = 0.0
+    xg[2::9] *= 1e-4
+    xg[2::9, 7] = -50.0
+    x = xg.reshape(k).astype(np.float32)
+    return synth.to_bf16_bits(x) if xdt == "bf16" else x
+
+
+@pytest.mark.parametrize("fmt,n,k,gs,xdt", [
+    (4, 512, 6144, 64, "bf16"), (4, 512, 16384, 0, "f32"), (4, 300, 2048, 32, "bf16"),
+    (1, 512, 6144, 0, "bf16"), (1, 300, 16384, 0, "f32"), (1, 64, 2048, 0, "bf16"),
+])
+def test_qgemv_one_token_wide_activation_range(q, oracle, fmt, n, k, gs, xdt):
+    """The integer-dot-product GEMV (one token, int4 k = 2048 m, int8 k = 1024 m)
+    within the bar for activations of very different magnitudes."""
+    print("qgemv wide-range fmt=%d n=%d k=%d gs=%d x=%s" % (fmt, n, k, gs, xdt), flush=True)
+    g = np.random.default_rng([9, fmt, n, k])
+    qw, s = synth.quant_matrix(g, fmt, n, k, gs)
+    x = _wide_range_x(9, k, xdt)
+    y = _run_gemv(q, fmt, n, k, gs, qw, s, x)
+    yr, nr = oracle.gemv(fmt, n, k, gs, qw, s, x)
+    assert norm_err(y, yr, nr) <= TOL
