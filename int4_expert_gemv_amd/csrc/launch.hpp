@@ -54,6 +54,7 @@ struct MoeDecodeArgs {
 // {1,2,3,4,6,8}); hipErrorNotSupported for other calls
 hipError_t launch_qgemv_q(int xdt, bool grouped, const GemvArgs& a, hipStream_t st);
 hipError_t launch_qgemv_q_pair(int xdt, bool grouped, const GemvArgs& a, const GemvArgs& b, hipStream_t st);
+hipError_t launch_qgemv_qb(int xdt, bool grouped, const GemvArgs& a, hipStream_t st);  // 2..8 activation rows
 // the same for int8 per-row weights (k = 1024 * {2,4,6,8,12,16}, v_dot4_i32_i8)
 hipError_t launch_qgemv_q8(int xdt, const GemvArgs& a, hipStream_t st);
 hipError_t launch_qgemv_q8_pair(int xdt, const GemvArgs& a, const GemvArgs& b, hipStream_t st);

@@ -135,6 +135,180 @@ __global__ __launch_bounds__(kQvThreads) void qgemv_q_kernel(GemvArgs a0, GemvAr
   }
 }
 
+// ---- small batch (qgemm_small), int4: NB activation rows per weight read --------
+// Same work split and register prefetch; x is staged once per workgroup as
+// bf16 pairs (activations 8q+i and 8q+4+i of a chunk in one word, the order
+// of the nibble pairs (w >> 4i) & 0x000F000F | 0x43004300 = bf16 (128+n)),
+// with the chunk's -136 * sum in an offset (fp32 activations as bf16 hi + lo,
+// |x - hi - lo| <= 2^-17 |x|).  A chunk's nibble pairs are built once per row
+// and used for every activation row; a row's x words are read once per chunk
+// for the wave's NU rows.  Rows of the batch past nb are skipped.
+template <int XT, int CB, int NB, int NU, bool GROUPED>
+__global__ __launch_bounds__(kQvThreads) void qgemv_b_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr bool SPLIT = XT == kF32;
+  constexpr int KCH = 64 * CB;  // chunks per row
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rb = (blockIdx.x * kQvWaves + wave) * NU;
+  const int nb = a.nb;
+  u32x4* xh = reinterpret_cast<u32x4*>(lds);                 // [NB][4][KCH]
+  u32x4* xl = xh + (SPLIT ? NB * 4 * KCH : 0);                // [NB][4][KCH] (fp32 x)
+  float* xo = reinterpret_cast<float*>(xh + (SPLIT ? 2 : 1) * NB * 4 * KCH);  // [NB][KCH]
+  // x first: one (row, chunk) per thread and step
+  for (int it = threadIdx.x; it < nb * KCH; it += kQvThreads) {
+    const int t = it / KCH, c = it - t * KCH;
+    float v[32];
+    if constexpr (XT == kBF16) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.ldx + c * 32);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x4 q4 = src[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * r + 2 * i] = __uint_as_float(q4[i] << 16);
+          v[8 * r + 2 * i + 1] = __uint_as_float(q4[i] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + (size_t)t * a.ldx + c * 32);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const f32x4 q4 = src[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * r + i] = q4[i];
+      }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = v[8 * q + i], a1 = v[8 * q + 4 + i];
+        const uint32_t h0 = f32_to_bf16_bits(a0), h1 = f32_to_bf16_bits(a1);
+        ph[i] = h0 | (h1 << 16);
+        if constexpr (SPLIT) {
+          const uint32_t l0 = f32_to_bf16_bits(a0 - bf16_bits_to_f32(h0)), l1 = f32_to_bf16_bits(a1 - bf16_bits_to_f32(h1));
+          pl[i] = l0 | (l1 << 16);
+          sum += (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
+        } else {
+          sum += bf16_bits_to_f32(h0) + bf16_bits_to_f32(h1);
+        }
+      }
+      xh[(t * 4 + q) * KCH + c] = ph;
+      if constexpr (SPLIT) xl[(t * 4 + q) * KCH + c] = pl;
+    }
+    xo[t * KCH + c] = -136.0f * sum;
+  }
+  // then every row of this wave, chunk-major
+  u32x4 wv[NU][CB];
+  float sv[NU][CB];
+  const bool won = rb < a.n;
+  if (won) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = lane + 64 * cb;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int r = min(rb + u, a.n - 1);
+        wv[u][cb] = ld_stream(a.q + (int64_t)r * a.row_bytes + (int64_t)c * 16);
+        sv[u][cb] = ld_stream(a.s + (int64_t)r * a.G + (GROUPED ? (c >> a.gshift) : 0));
+      }
+    }
+  }
+  lds_barrier();
+  if (!won) return;
+  const NibConst nk = nib_const();
+  float acc[NB][NU];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[t][u] = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int c = lane + 64 * cb;
+    uint32_t pr[NU][16];
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[u][q * 4 + i] = nib_pair(wv[u][cb][q] >> (4 * i), nk);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      if (t < nb) {
+        u32x4 hq[4], lq[SPLIT ? 4 : 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hq[q] = xh[(t * 4 + q) * KCH + c];
+          if constexpr (SPLIT) lq[q] = xl[(t * 4 + q) * KCH + c];
+        }
+        const float off = xo[t * KCH + c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          float tt = off;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              tt = dot2(pr[u][q * 4 + i], hq[q][i], tt);
+              if constexpr (SPLIT) tt = dot2(pr[u][q * 4 + i], lq[q][i], tt);
+            }
+          acc[t][u] = __builtin_fmaf(sv[u][cb], tt, acc[t][u]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+    if (t < nb) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const float yv = group_sum<64>(acc[t][u]);
+        if (lane == 0 && rb + u < a.n) a.y[(int64_t)t * a.ldy + rb + u] = yv;
+      }
+    }
+}
+
+template <int XT, int CB, int NB, bool GROUPED>
+hipError_t launch_qvb(const GemvArgs& a, hipStream_t st) {
+  constexpr int KCH = 64 * CB;
+  const size_t lds = (size_t)NB * KCH * (4 * 16 * (XT == kF32 ? 2 : 1) + 4);
+  if (lds > (size_t)kLdsMax) return hipErrorNotSupported;
+  constexpr int kCus = 256;
+  const int need = (a.n + kCus * kQvWaves - 1) / (kCus * kQvWaves);
+  auto go = [&](auto nu_tag) {
+    constexpr int NU = decltype(nu_tag)::value;
+    const int rows = kQvWaves * NU;
+    hipLaunchKernelGGL((qgemv_b_kernel<XT, CB, NB, NU, GROUPED>), dim3((a.n + rows - 1) / rows), dim3(kQvThreads),
+                       lds, st, a);
+    return hipGetLastError();
+  };
+  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 2 || CB > 4) return go(std::integral_constant<int, 2>{});
+  return go(std::integral_constant<int, 3>{});
+}
+
+template <int XT, int CB, bool GROUPED>
+hipError_t launch_qvb_nb(const GemvArgs& a, hipStream_t st) {
+  if (a.nb <= 2) return launch_qvb<XT, CB, 2, GROUPED>(a, st);
+  if (a.nb <= 4) return launch_qvb<XT, CB, 4, GROUPED>(a, st);
+  return launch_qvb<XT, CB, 8, GROUPED>(a, st);
+}
+
+template <int XT, bool GROUPED>
+hipError_t launch_qvb_cb(const GemvArgs& a, hipStream_t st) {
+  switch (a.k / 2048) {
+    case 1: return launch_qvb_nb<XT, 1, GROUPED>(a, st);
+    case 2: return launch_qvb_nb<XT, 2, GROUPED>(a, st);
+    case 3: return launch_qvb_nb<XT, 3, GROUPED>(a, st);
+    case 4: return launch_qvb_nb<XT, 4, GROUPED>(a, st);
+    case 6: return launch_qvb_nb<XT, 6, GROUPED>(a, st);
+    case 8: return launch_qvb_nb<XT, 8, GROUPED>(a, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 // ---- int8 per-row weights ------------------------------------------------------
 // The same scheme with v_dot4_i32_i8: the integers X of a group of 16
 // activations (as above, |X| <= 30567) are written with two balanced base-256
@@ -374,6 +548,15 @@ hipError_t launch_qgemv_q8_pair(int xdt, const GemvArgs& a, const GemvArgs& b, h
   if (!QM_QGEMV_Q || a.n < 1 || b.n < 1 || a.k != b.k || a.k % 1024 || ((uintptr_t)a.x & 15) != 0)
     return hipErrorNotSupported;
   return xdt == kBF16 ? launch_qv8_cb<kBF16>(a, b, true, st) : launch_qv8_cb<kF32>(a, b, true, st);
+}
+
+// int4, 2..8 activation rows (qgemm_small), k = 2048 * {1,2,3,4,6,8} with the
+// staged rows fitting in LDS; hipErrorNotSupported otherwise
+hipError_t launch_qgemv_qb(int xdt, bool grouped, const GemvArgs& a, hipStream_t st) {
+  if (!QM_QGEMV_Q || a.n < 1 || a.nb < 2 || a.nb > 8 || a.k % 2048 || ((uintptr_t)a.x & 15) != 0)
+    return hipErrorNotSupported;
+  if (xdt == kBF16) return grouped ? launch_qvb_cb<kBF16, true>(a, st) : launch_qvb_cb<kBF16, false>(a, st);
+  return grouped ? launch_qvb_cb<kF32, true>(a, st) : launch_qvb_cb<kF32, false>(a, st);
 }
 
 // two int4 matrices of one x in one launch (same k and grouping)

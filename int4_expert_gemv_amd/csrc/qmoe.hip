@@ -116,6 +116,11 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
                                          static_cast<hipStream_t>(stream));
     if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
   }
+  if (w->fmt == QM_FMT_INT4 && batch > 1) {
+    const hipError_t eq = launch_qgemv_qb(xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a,
+                                          static_cast<hipStream_t>(stream));
+    if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   if (w->fmt == QM_FMT_INT8_ROW && batch == 1) {
     const hipError_t eq = launch_qgemv_q8(xdt, a, static_cast<hipStream_t>(stream));
     if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
