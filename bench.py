@@ -188,7 +188,8 @@ def bench_moe(args, E, H, I):
     torch.cuda.synchronize()
     gu_ms = gs0.elapsed_time(gs1) / args.steps
 
-    # the two stage entry points on the last step, untimed, must agree bit for bit with the layer call
+    # the two stage entry points on the last step, untimed (the layer call may
+    # run them as one launch: then the two agree to fp32 rounding, not bit for bit)
     y2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
     last = n_steps - 1
     qmoe.moe_gate_up(e, x_d[last], ids_d[last], h)
@@ -196,10 +197,11 @@ def bench_moe(args, E, H, I):
     torch.cuda.synchronize()
     same = bool(torch.equal(y2, y[last]))
 
-    # parity of the last step against the oracle
+    # parity of the last step (layer call and stage calls) against the oracle
     o = ref.oracle()
     yr, _, nr = o.moe_ffn(ex, x_h[last], ids_h[last], w_h[last])
     err = ref.max_norm_err(y[last].cpu().numpy(), yr, nr)
+    err_stages = ref.max_norm_err(y2.cpu().numpy(), yr, nr)
 
     ebytes = expert_bytes(fmt, H, I, gs)
     uniq = [len(np.unique(ids_h[args.warmup + j])) for j in range(args.steps)]
@@ -241,7 +243,8 @@ def bench_moe(args, E, H, I):
                      "traffic": counter_traffic("moe_gate_up_%s_counters" % tag),
                      "kernel": "fused gate+up+SiLU (moe_gate_up stage)", "us_per_launch": round(gu_ms * 1e3, 3),
                      "bytes_per_launch": int(gu_bytes)},
-        "parity": {"max_norm_err": err, "tol": 2e-4, "stage_entry_points_identical": same},
+        "parity": {"max_norm_err": err, "tol": 2e-4, "stage_entry_points_max_norm_err": err_stages,
+                   "stage_entry_points_identical": same},
         "cpu_baseline": cpu,
         **({"shared_expert": {"separate_call_us_per_layer": round(separate_us, 3),
                               "folded_us_per_layer": round(ms_step * 1e3, 3)}} if nsh else {}),

@@ -28,7 +28,7 @@ def sources():
 
 # The sources the single-token decode kernels are built from (the fused
 # gate+up kernel whose counters the bench reports, and the down kernel).
-DECODE_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_t1_lds.hpp", "moe_t1_q.hpp", "moe_t1_impl.hpp",
+DECODE_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_t1_lds.hpp", "moe_t1_q.hpp", "moe_t1_s.hpp", "moe_t1_impl.hpp",
                   "moe_decode_impl.hpp", "moe_decode.hip", "moe_decode_i4_bf16.hip", "qmoe.hip")
 
 

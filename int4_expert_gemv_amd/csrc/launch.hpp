@@ -48,6 +48,8 @@ struct MoeDecodeArgs {
   uint32_t* hq;        // workspace: h as digit words [T*k][I/16][8] (single-token int4 kernels)
   float* hqs;          // workspace: their factors [T*k][I/16]
   int hq_ready;        // hq already holds the digits of h (written by the gate+up kernel)
+  uint64_t* flags;     // workspace: one 64-bit flag per tile of h (one-launch layer)
+  uint64_t nonce;      // value the flags take in this call (fresh per call)
 };
 
 // qgemv_q.hip: single-token int4 GEMV on integer dot products (k = 2048 *
@@ -109,6 +111,10 @@ QM_DECL_MOE(moe_gate_up_i8_f32_r)
 QM_DECL_MOE(moe_down_i4_g)
 QM_DECL_MOE(moe_down_i4_r)
 QM_DECL_MOE(moe_down_i8_r)
+QM_DECL_MOE(moe_ffn_i4_bf16_g)  // the one-launch layer (hipErrorNotSupported: not taken)
+QM_DECL_MOE(moe_ffn_i4_bf16_r)
+QM_DECL_MOE(moe_ffn_i4_f32_g)
+QM_DECL_MOE(moe_ffn_i4_f32_r)
 #undef QM_DECL_MOE
 
 // moe_decode.hip
@@ -116,6 +122,9 @@ hipError_t launch_moe_gate_up(int fmt, int xdt, bool grouped, const MoeDecodeArg
 hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 // true when launch_moe_gate_up with these arguments also writes the digits of h to a.hq
 bool moe_gate_up_writes_digits(int fmt, const MoeDecodeArgs& a);
+// the whole decode layer in one launch when the one-launch kernel takes the
+// call; hipErrorNotSupported otherwise (the caller then runs the two stages)
+hipError_t launch_moe_ffn_layer(int fmt, int xdt, bool grouped, const MoeDecodeArgs& a, hipStream_t st);
 
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
 // (or row length, per-row scales) is a multiple of 64 with at most 96 groups

@@ -19,6 +19,12 @@ hipError_t launch_moe_down(int fmt, bool grouped, const MoeDecodeArgs& a, hipStr
   return moe_down_i8_r(a, st);
 }
 
+hipError_t launch_moe_ffn_layer(int fmt, int xdt, bool grouped, const MoeDecodeArgs& a, hipStream_t st) {
+  if (fmt != 4) return hipErrorNotSupported;
+  if (xdt == 1) return grouped ? moe_ffn_i4_bf16_g(a, st) : moe_ffn_i4_bf16_r(a, st);
+  return grouped ? moe_ffn_i4_f32_g(a, st) : moe_ffn_i4_f32_r(a, st);
+}
+
 bool moe_gate_up_writes_digits(int fmt, const MoeDecodeArgs& a) {
   return fmt == 4 && a.hq != nullptr && q_gate_up_ok(a);
 }

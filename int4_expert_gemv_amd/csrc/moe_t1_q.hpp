@@ -126,18 +126,19 @@ __device__ __forceinline__ float q_chunk(const u32x4& w, const u32x4 (&xd)[4], c
 }
 
 // ---- gate + up ----------------------------------------------------------------
-// H = 64 * CB * 32 (a lane owns chunks lane + 64 cb of every row).  Block b:
-// routed pair b / ntile, rows [RPB * (b % ntile), +RPB); wave w takes rows
-// w, w + kWaves, ... of the tile, one row of gate and up per unit.
+// One row of gate and one of up of a routed expert per unit, streamed through
+// an LDS ring of D slots per wave.
 template <int CB, bool PS>
 __host__ __device__ constexpr int q_gu_slot() {
   return 2 * CB * 1024 + (PS ? 1024 : 2 * CB * 256);
 }
 
-template <int XT, int CB, int RPB, int D, bool GROUPED, bool PS>
-__global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ __attribute__((aligned(16))) float s_h[RPB];
+// One gate+up tile: routed pair p, intermediate rows r0 .. r0+RPB-1 (h to
+// a.h when set, its digits to a.hq when set; COHERENT: the digits go out as
+// device-coherent stores, for readers in other workgroups of the same
+// launch).  Returns false for a pair with an invalid expert id (nothing done).
+template <int XT, int CB, int RPB, int D, bool GROUPED, bool PS, bool COHERENT>
+__device__ __forceinline__ bool gu_tile(const MoeDecodeArgs& a, char* lds, float* s_h, int p, int r0) {
   constexpr int M = 2;
   constexpr int NW = M * CB;              // 1 KiB weight blocks per unit
   constexpr int U = NW + (PS ? 1 : NW);   // VMEM operations per unit
@@ -146,10 +147,8 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
   static_assert(!PS || GROUPED, "packed scales need grouped scales");
   static_assert(RPB % 16 == 0 && RPB % kWaves == 0, "tile of whole digit groups");
   const ExpertArgs& ex = a.ex;
-  const int ntile = ex.I / RPB;
-  const int p = blockIdx.x / ntile, r0 = (blockIdx.x - p * ntile) * RPB;  // pair p = token * topk + slot
   const int id = a.ids[p];
-  if (id < 0 || id >= ex.E) return;  // the down kernel skips this slot
+  if (id < 0 || id >= ex.E) return false;  // the down kernel skips this slot
   const char* xt = static_cast<const char*>(a.x) + (size_t)(p / a.topk) * ex.H * (XT == kBF16 ? 2 : 4);
   const int e = uniform(id);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
       if (a.h) a.h[(int64_t)p * ex.I + r0 + rl] = hv;
     }
   }
-  if (!a.hq) return;
+  if (!a.hq) return true;
   __syncthreads();
   // digits of the tile's h: eight threads per group of 16, one word each
   // (shift and carry constant of digit d computed, not branched on)
@@ -294,9 +293,28 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs
       }
     }
     const int64_t gi = (int64_t)p * (ex.I / 16) + r0 / 16 + g;  // global group index
-    a.hq[gi * 8 + j * 4 + d] = w;
-    if ((threadIdx.x & 7) == 0) a.hqs[gi] = ldexpf(1.f, E - 15);
+    if constexpr (COHERENT) {
+      __hip_atomic_store(a.hq + gi * 8 + j * 4 + d, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((threadIdx.x & 7) == 0)
+        __hip_atomic_store(a.hqs + gi, ldexpf(1.f, E - 15), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      a.hq[gi * 8 + j * 4 + d] = w;
+      if ((threadIdx.x & 7) == 0) a.hqs[gi] = ldexpf(1.f, E - 15);
+    }
   }
+  return true;
+}
+
+// H = 64 * CB * 32 (a lane owns chunks lane + 64 cb of every row).  Block b:
+// routed pair b / ntile (pair p = token * topk + slot), rows
+// [RPB * (b % ntile), +RPB); wave w takes rows w, w + kWaves, ... of the tile.
+template <int XT, int CB, int RPB, int D, bool GROUPED, bool PS>
+__global__ __launch_bounds__(kThreads) void moe_gate_up_t1q_kernel(MoeDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(16))) float s_h[RPB];
+  const int ntile = a.ex.I / RPB;
+  const int p = blockIdx.x / ntile, r0 = (blockIdx.x - p * ntile) * RPB;
+  gu_tile<XT, CB, RPB, D, GROUPED, PS, false>(a, lds, s_h, p, r0);
 }
 
 // h (fp32 [T*k][I]) -> digit words and factors, one thread per group of 16;

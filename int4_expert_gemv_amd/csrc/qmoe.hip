@@ -5,6 +5,9 @@
 // "qwen36: Vulkan expert tier, and staged device-local uploads" keeps the
 // caller's output untouched when the GPU path refuses a request).
 #include "qmoe.h"
+#include <atomic>
+#include <chrono>
+
 #include "launch.hpp"
 
 #include <limits.h>
@@ -165,7 +168,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t decode_workspace(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k;
-  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256) + align_up(P * I * 2, 256) + align_up(P * I / 4, 256);
+  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256) + align_up(P * I * 2, 256) + align_up(P * I / 4, 256) +
+         align_up(P * ((I + 15) / 16) * 8, 256);
 }
 
 ExpertArgs expert_args(const qm_experts* ex) {
@@ -188,8 +192,22 @@ ExpertArgs expert_args(const qm_experts* ex) {
   return e;
 }
 
+// A value no earlier call has used (splitmix64 of a process-wide counter
+// seeded from the clock), never 0: the one-launch layer's tile flags take it,
+// so flags left in a workspace by earlier calls never read as set.
+uint64_t call_nonce() {
+  static std::atomic<uint64_t> ctr{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() *
+                                   0x9E3779B97F4A7C15ull};
+  uint64_t z = ctr.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z ? z : 1;
+}
+
 // Decode workspace: h [T*k][I] fp32, per-pair down outputs [T*k][H] fp32, h as
-// digit words [T*k][I/16][8] u32 and their factors [T*k][I/16] fp32.
+// digit words [T*k][I/16][8] u32 and their factors [T*k][I/16] fp32, tile
+// flags [T*k][I/16] u64.
 MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32_t* ids, const float* w, int k,
                           float* y, void* workspace) {
   MoeDecodeArgs a{};
@@ -204,6 +222,8 @@ MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32
     a.pout = reinterpret_cast<float*>(ws + align_up(P * e.I * 4, 256));
     a.hq = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.pout) + align_up(P * e.H * 4, 256));
     a.hqs = reinterpret_cast<float*>(reinterpret_cast<char*>(a.hq) + align_up(P * e.I * 2, 256));
+    a.flags = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.hqs) + align_up(P * e.I / 4, 256));
+    a.nonce = call_nonce();
   }
   a.y = y;
   a.T = T;
@@ -345,9 +365,12 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
       MoeDecodeArgs a = decode_args(e, static_cast<const char*>(x) + (size_t)t0 * xs, nt,
                                     topk_ids + (size_t)t0 * top_k, topk_w + (size_t)t0 * top_k, top_k,
                                     y + (size_t)t0 * ex->hidden, workspace);
-      a.hq_ready = moe_gate_up_writes_digits(ex->fmt, a) ? 1 : 0;
-      err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
-      if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
+      err = launch_moe_ffn_layer(ex->fmt, x_dtype, grouped, a, s);
+      if (err == hipErrorNotSupported) {
+        a.hq_ready = moe_gate_up_writes_digits(ex->fmt, a) ? 1 : 0;
+        err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
+        if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
+      }
     }
   }
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
