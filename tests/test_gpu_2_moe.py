@@ -161,3 +161,32 @@ def test_moe_one_token_stages_match_layer(q):
     q.moe_down(e, h, idd, wd, y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("H,k,bad", [(2048, 8, False), (2048, 8, True), (2048, 4, False), (4096, 8, True)])
+def test_moe_small_experts_one_launch(q, oracle, H, k, bad):
+    """inter 512, one token: the one-launch layer (tile flags with a per-call
+    nonce), with fewer slots, invalid and duplicate ids, hidden 4096; two calls
+    on one workspace give identical y (the flags of the first never satisfy
+    the second)."""
+    E, I, T = 24, 512, 1
+    print("moe one-launch H=%d k=%d bad=%s" % (H, k, bad), flush=True)
+    ids, w = _routing(16 + H + k, T, E, k)
+    if bad:
+        ids[0, 1] = -1          # skipped
+        ids[0, 3] = E + 5       # skipped
+        ids[0, 6] = ids[0, 0]   # the same expert twice: summed
+    ex = synth.expert_set(17, 4, E, H, I, 64)
+    d = upload_experts(ex)
+    x = synth.activations(np.random.default_rng(18), (T, H), "bf16")
+    e = q.experts(4, 64, d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
+    ws = torch.empty(q.moe_expert_ffn_workspace(e, T, k), dtype=torch.uint8, device="cuda")
+    ys = []
+    for _ in range(2):
+        y = torch.full((T, H), float("nan"), device="cuda")
+        q.moe_expert_ffn(e, dev(x), dev(ids), dev(w), y, ws)
+        torch.cuda.synchronize()
+        ys.append(host(y))
+    assert np.array_equal(ys[0], ys[1])
+    yr, _, nr = oracle.moe_ffn(ex, x, ids, w)
+    assert norm_err(ys[0], yr, nr) <= TOL
