@@ -18,8 +18,12 @@
  * Conventions shared by every entry point
  *  - Pointers marked "device" are HIP device pointers; the caller owns every
  *    buffer (weights, activations, outputs, workspace).  The library keeps no
- *    pointer after a call returns, allocates nothing and holds no global
- *    state, so calls are reentrant.
+ *    pointer after a call returns and allocates nothing.  Its only global
+ *    state is a thread-safe call counter (the nonce of the one-launch decode
+ *    layer's tile flags) and a per-device occupancy figure cached on first
+ *    use, so calls are reentrant.  Two calls must not share one workspace
+ *    while both are in flight (on different streams), as for any scratch
+ *    buffer.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls only enqueue work and return; results are ready when the stream
  *    reaches them.  Time them with events on that stream.
