@@ -291,9 +291,26 @@ hipError_t launch_qvb(const GemvArgs& a, hipStream_t st) {
 
 template <int XT, int CB, bool GROUPED>
 hipError_t launch_qvb_nb(const GemvArgs& a, hipStream_t st) {
-  if (a.nb <= 2) return launch_qvb<XT, CB, 2, GROUPED>(a, st);
-  if (a.nb <= 4) return launch_qvb<XT, CB, 4, GROUPED>(a, st);
-  return launch_qvb<XT, CB, 8, GROUPED>(a, st);
+  // activation rows one launch stages: the batch rounded up to 2, 4 or 8,
+  // fewer when their staging would not fit in LDS -- then the batch runs as
+  // several launches over row groups (each reads the weights again; at these
+  // batch sizes the arithmetic, not the weight stream, is the bound)
+  constexpr size_t per = (size_t)64 * CB * (4 * 16 * (XT == kF32 ? 2 : 1) + 4);  // LDS bytes per row
+  int nbs = a.nb <= 2 ? 2 : (a.nb <= 4 ? 4 : 8);
+  while (nbs > 2 && (size_t)nbs * per > (size_t)kLdsMax) nbs /= 2;
+  if ((size_t)nbs * per > (size_t)kLdsMax) return hipErrorNotSupported;
+  const size_t xsz = XT == kBF16 ? 2 : 4;
+  for (int t0 = 0; t0 < a.nb; t0 += nbs) {
+    GemvArgs b = a;
+    b.x = static_cast<const char*>(a.x) + (size_t)t0 * a.ldx * xsz;
+    b.y = a.y + (size_t)t0 * a.ldy;
+    b.nb = a.nb - t0 < nbs ? a.nb - t0 : nbs;
+    const hipError_t e = nbs == 2 ? launch_qvb<XT, CB, 2, GROUPED>(b, st)
+                                  : (nbs == 4 ? launch_qvb<XT, CB, 4, GROUPED>(b, st)
+                                              : launch_qvb<XT, CB, 8, GROUPED>(b, st));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int XT, bool GROUPED>
