@@ -22,6 +22,13 @@
 
 namespace qm {
 
+#ifndef QM_Q4_CAP
+#define QM_Q4_CAP 8  // most rows per wave of the int4 GEMV
+#endif
+#ifndef QM_Q8_CAP16
+#define QM_Q8_CAP16 1  // rows per wave for int8 rows of 16384: one (more, smaller workgroups)
+#endif
+
 constexpr int kQvWaves = 8;
 constexpr int kQvThreads = 64 * kQvWaves;
 
@@ -473,7 +480,7 @@ hipError_t launch_qv8(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream
   constexpr int kCus = 256;
   const int rows_all = a.n + (pair ? b.n : 0);
   const int need = (rows_all + kCus * kQvWaves - 1) / (kCus * kQvWaves);
-  constexpr int cap = CB <= 4 ? 8 : (CB <= 8 ? 4 : 2);
+  constexpr int cap = CB <= 4 ? 8 : (CB <= 8 ? 4 : QM_Q8_CAP16);
   const size_t lds = (size_t)1024 * CB * 2 + (size_t)1024 * CB / 4;
   auto go = [&](auto nu_tag) {
     constexpr int NU = decltype(nu_tag)::value;
@@ -484,7 +491,7 @@ hipError_t launch_qv8(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream
                        nba);
     return hipGetLastError();
   };
-  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 1 || cap <= 1) return go(std::integral_constant<int, 1>{});
   if (need <= 2 || cap <= 2) return go(std::integral_constant<int, 2>{});
   if (need <= 3) return go(std::integral_constant<int, 3>{});
   if (need <= 4 || cap <= 4) return go(std::integral_constant<int, 4>{});
@@ -511,7 +518,7 @@ hipError_t launch_qv(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_
   constexpr int kCus = 256;
   const int rows_all = a.n + (pair ? b.n : 0);
   const int need = (rows_all + kCus * kQvWaves - 1) / (kCus * kQvWaves);
-  constexpr int cap = CB <= 3 ? 8 : (CB <= 4 ? 6 : 4);
+  constexpr int cap = CB <= 3 ? (QM_Q4_CAP < 8 ? QM_Q4_CAP : 8) : (CB <= 4 ? (QM_Q4_CAP < 6 ? QM_Q4_CAP : 6) : (QM_Q4_CAP < 4 ? QM_Q4_CAP : 4));
   const size_t lds = (size_t)2048 * CB * 2 + (size_t)2048 * CB / 4;
   auto go = [&](auto nu_tag) {
     constexpr int NU = decltype(nu_tag)::value;
@@ -522,7 +529,8 @@ hipError_t launch_qv(const GemvArgs& a, const GemvArgs& b, bool pair, hipStream_
                        pair ? b : a, nba);
     return hipGetLastError();
   };
-  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 1 || cap <= 1) return go(std::integral_constant<int, 1>{});
+  if (cap <= 2) return go(std::integral_constant<int, (cap < 2 ? 1 : 2)>{});
   if (need <= 2) return go(std::integral_constant<int, 2>{});
   if (need <= 3 || cap <= 3) return go(std::integral_constant<int, (cap < 3 ? cap : 3)>{});
   if (need <= 4 || cap <= 4) return go(std::integral_constant<int, 4>{});
