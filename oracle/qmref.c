@@ -300,7 +300,9 @@ int qmref_moe_ffn(const qmref_experts *ex, const void *x, int x_dtype, int n_tok
     }
     for (int c = 0; c < H; ++c) {
       double v = x_at(x, x_dtype, (int64_t)t * H + c);
+#if QMREF_MUTANT != 14 /* mutant 14: fp32 x not rounded in the bf16 activation mode */
       if ((flags & QMREF_BF16_ACT) && x_dtype == QMREF_F32) v = qmref_round_bf16(v);
+#endif
       xt[c] = v;
     }
     for (int j = 0; j < top_k; ++j) {
@@ -336,7 +338,13 @@ int qmref_moe_ffn(const qmref_experts *ex, const void *x, int x_dtype, int n_tok
 #else
         yt[i] += wt * o[i];
 #endif
+#if QMREF_MUTANT == 12
+        if (nt) nt[i] += wt * on[i]; /* mutant: sign of the routing weight kept */
+#elif QMREF_MUTANT == 13
+        if (nt) nt[i] += on[i]; /* mutant: routing weight left out of the normaliser */
+#else
         if (nt) nt[i] += fabs(wt) * on[i];
+#endif
       }
     }
   }

@@ -59,12 +59,18 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def moe(ex, x, ids, w):
-    """Dense float64 MoE: y_t = sum_j w_tj * D_e (silu(G_e x_t) * (U_e x_t))."""
+def moe(ex, x, ids, w, round_h=None):
+    """Dense float64 MoE: y_t = sum_j w_tj * D_e (silu(G_e x_t) * (U_e x_t)).
+
+    Returns (y, norm) with norm[t][i] = sum_j |w_tj| * sum_m |D_e[i][m] h_m|,
+    the per-output sum of absolute terms of the final contraction (the
+    scale the parity bar is measured against).  round_h, when given, is
+    applied to each hidden vector before the down projection."""
     H, I, fmt, gs = ex["hidden"], ex["inter"], ex["fmt"], ex["gs"]
     x = np.asarray(x, dtype=np.float64)
     T, k = ids.shape
     y = np.zeros((T, H))
+    nrm = np.zeros((T, H))
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
@@ -74,5 +80,8 @@ def moe(ex, x, ids, w):
             U = np.prod(dense(fmt, ex["up_q"][e], ex["up_s"][e], H, gs), axis=0)
             D = np.prod(dense(fmt, ex["down_q"][e], ex["down_s"][e], I, gs), axis=0)
             h = silu(G @ x[t]) * (U @ x[t])
+            if round_h is not None:
+                h = round_h(h)
             y[t] += float(w[t, j]) * (D @ h)
-    return y
+            nrm[t] += abs(float(w[t, j])) * (np.abs(D) @ np.abs(h))
+    return y, nrm

@@ -170,13 +170,36 @@ def pin_bruteforce_gemv(o, fmt, n, k, gs, xdt, seed=3):
 
 
 def pin_bruteforce_moe(o, fmt, gs, T=3, E=5, H=128, I=64, k=3, seed=4):
+    """y and the parity normaliser against the dense numpy restatement, with
+    routing weights of both signs (the normaliser takes |w|)."""
     ex = synth.expert_set(seed, fmt, E, H, I, gs)
     g = np.random.default_rng([seed, 99])
     x = synth.activations(g, (T, H), "f32")
     ids, w = synth.uniform_routing(g, T, E, k)
+    w = (w * np.where(g.random(w.shape) < 0.5, -1.0, 1.0) * g.uniform(0.5, 3.0, w.shape)).astype(np.float32)
     y, _, nrm = o.moe_ffn(ex, x, ids, w)
-    yb = bf.moe(ex, x, ids, w)
-    assert np.all(np.abs(y - yb) <= 1e-12 * nrm), np.max(np.abs(y - yb) / nrm)
+    yb, nb = bf.moe(ex, x, ids, w)
+    assert np.all(np.abs(y - yb) <= 1e-12 * nb), np.max(np.abs(y - yb) / nb)
+    assert np.all(np.abs(nrm - nb) <= 1e-12 * nb), np.max(np.abs(nrm - nb) / nb)
+
+
+def pin_bf16_act(o, T=2, E=4, H=64, I=32, k=2, seed=14):
+    """Prefill precision mode with fp32 activations that bf16 cannot hold:
+    the oracle must give exactly what it gives for the same x rounded to
+    bf16 by torch, and match the dense restatement with x and every hidden
+    vector rounded to the nearest bf16 (exact table search)."""
+    ex = synth.expert_set(seed, 4, E, H, I, 64)
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((T, H)) * (1.0 + 2.0 ** -12)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xr = (xb.astype(np.uint32) << 16).view(np.float32)
+    assert not np.array_equal(xr, x)  # the rounding is visible
+    ids, w = synth.uniform_routing(g, T, E, k)
+    y1, h1, n1 = o.moe_ffn(ex, x, ids, w, flags=ref.BF16_ACT, want_h=True)
+    y2, h2, n2 = o.moe_ffn(ex, xb, ids, w, flags=ref.BF16_ACT, want_h=True)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2) and np.array_equal(n1, n2)
+    yb, nb = bf.moe(ex, xr, ids, w, round_h=lambda h: np.array([_exact_bf16(v) for v in h]))
+    assert np.all(np.abs(y1 - yb) <= 1e-12 * nb), np.max(np.abs(y1 - yb) / nb)
 
 
 def pin_rmsnorm(o):
@@ -265,6 +288,7 @@ def run_battery(o):
     pin_bruteforce_gemv(o, 1, 5, 48, 0, "bf16")
     pin_bruteforce_moe(o, 4, 64)
     pin_bruteforce_moe(o, 1, 0)
+    pin_bf16_act(o)
 
 
 # --------------------------------------------------------------------------
@@ -529,7 +553,10 @@ def test_moe_bf16_mode_rounds_h(oracle):
 
 MUTANTS = {1: "high nibble first", 2: "offset 7", 3: "wrong group index", 4: "silu sign",
            5: "gate/up swapped", 6: "routing list transposed", 7: "routing weight dropped",
-           8: "bf16 truncation", 9: "int8 unsigned", 10: "rmsnorm sum for mean", 11: "int3 offset 3"}
+           8: "bf16 truncation", 9: "int8 unsigned", 10: "rmsnorm sum for mean", 11: "int3 offset 3",
+           12: "normaliser keeps the sign of the routing weight",
+           13: "routing weight left out of the normaliser",
+           14: "fp32 x not rounded in the bf16 activation mode"}
 
 
 def test_real_oracle_passes_battery(oracle):
