@@ -86,7 +86,8 @@ typedef enum {
   QM_ERR_INVALID = -1,     /* malformed argument: null pointer, negative size, bad enum */
   QM_ERR_UNSUPPORTED = -2, /* well-formed but outside what the GPU path implements */
   QM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  QM_ERR_LAUNCH = -4       /* a HIP launch failed */
+  QM_ERR_LAUNCH = -4,      /* a HIP launch failed */
+  QM_ERR_TOO_LARGE = -5    /* needs more scratch than moe_expert_ffn_noalloc holds */
 } qm_status;
 
 typedef enum { QM_FMT_INT8_ROW = 1, QM_FMT_INT4 = 4, QM_FMT_INT3 = 5 } qm_fmt;
@@ -96,7 +97,8 @@ enum {
   QM_SMALL_MAX = 8,           /* largest batch of qgemm_small                       */
   QM_TOPK_MAX = 32,           /* largest top_k of moe_expert_ffn                    */
   QM_DECODE_MAX_TOKENS = 8,   /* moe_expert_ffn runs the decode kernels up to this  */
-  QM_K_MAX = 1 << 20          /* largest reduction length                           */
+  QM_K_MAX = 1 << 20,         /* largest reduction length                           */
+  QM_NOALLOC_SCRATCH_BYTES = 32 << 20  /* fixed scratch of moe_expert_ffn_noalloc, per GPU */
 };
 
 /* which kernels moe_expert_ffn_path runs */
@@ -216,6 +218,24 @@ QM_API int moe_gate_up(const qm_experts *ex, const void *x, int32_t x_dtype, int
 QM_API int moe_down(const qm_experts *ex, const float *h, int32_t n_tokens, const int32_t *topk_ids,
                     const float *topk_w, int32_t top_k, float *y, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* moe_expert_ffn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as moe_expert_ffn without the workspace: the
+ * scratch it needs comes from a fixed device array of
+ * QM_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends.  Nothing is allocated by the call (no hipMalloc, no
+ * allocating library routine); the array's device address is looked up once
+ * per GPU on the first call made with that GPU current.  A call that needs
+ * more scratch than that (moe_expert_ffn_workspace() > the limit: large
+ * prefill batches) returns QM_ERR_TOO_LARGE before anything is enqueued.
+ * Every call on a GPU uses that GPU's one array, whose contents carry over
+ * from the previous call: calls that can overlap on one GPU (several
+ * streams, several host threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero.                    */
+QM_API int moe_expert_ffn_noalloc(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
+                                  const int32_t *topk_ids, const float *topk_w, int32_t top_k, float *y,
+                                  void *stream);
 
 /* Static text for a qm_status value. */
 QM_API const char *qm_strerror(int status);

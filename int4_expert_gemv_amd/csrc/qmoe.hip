@@ -7,10 +7,17 @@
 #include "qmoe.h"
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "launch.hpp"
 
 #include <limits.h>
+
+// Scratch of the allocation-free entry point: a fixed device array, one copy
+// per GPU.  In host code `scratch` names a host-side stand-in, never the
+// device memory; its device address is looked up per device (with that
+// device current) and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[QM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -241,6 +248,28 @@ int moe_grouping(const qm_experts* ex, bool* grouped) {
   return QM_OK;
 }
 
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current; nullptr if HIP cannot give it.
+void* scratch_ptr() {
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return nullptr;
+    ptrs[dev].store(a, std::memory_order_release);
+    p = a;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +281,7 @@ const char* qm_strerror(int status) {
     case QM_ERR_UNSUPPORTED: return "unsupported shape, format or alignment for the GPU path";
     case QM_ERR_WORKSPACE: return "workspace missing or too small";
     case QM_ERR_LAUNCH: return "HIP kernel launch failed";
+    case QM_ERR_TOO_LARGE: return "needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -425,3 +455,25 @@ int moe_expert_ffn(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t
 }
 
 }  // extern "C"
+
+extern "C" int moe_expert_ffn_noalloc(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens,
+                                      const int32_t* topk_ids, const float* topk_w, int32_t top_k, float* y,
+                                      void* stream) {
+  // argument checks first (host only), so a malformed call reports what is
+  // wrong with it rather than its size
+  if (x_dtype != QM_F32 && x_dtype != QM_BF16) return QM_ERR_INVALID;
+  if (n_tokens < 0 || top_k < 1) return QM_ERR_INVALID;
+  const int st = check_experts(ex);
+  if (st == QM_ERR_INVALID) return st;
+  if (n_tokens == 0) return QM_OK;
+  if (!x || !topk_ids || !topk_w || !y) return QM_ERR_INVALID;
+  if (st != QM_OK) return st;
+  if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
+  const size_t need = moe_expert_ffn_workspace(ex, n_tokens, top_k);
+  if (need == 0) return QM_ERR_INVALID;
+  if (need > (size_t)QM_NOALLOC_SCRATCH_BYTES) return QM_ERR_TOO_LARGE;
+  void* ws = scratch_ptr();
+  if (!ws) return QM_ERR_LAUNCH;
+  return moe_expert_ffn_path(ex, x, x_dtype, n_tokens, topk_ids, topk_w, top_k, y, ws,
+                             (size_t)QM_NOALLOC_SCRATCH_BYTES, stream, QM_PATH_AUTO);
+}

@@ -13,14 +13,15 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
-QM_OK, QM_ERR_INVALID, QM_ERR_UNSUPPORTED, QM_ERR_WORKSPACE, QM_ERR_LAUNCH = 0, -1, -2, -3, -4
+QM_OK, QM_ERR_INVALID, QM_ERR_UNSUPPORTED, QM_ERR_WORKSPACE, QM_ERR_LAUNCH, QM_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 QM_FMT_INT8_ROW, QM_FMT_INT4 = 1, 4
 QM_F32, QM_BF16 = 0, 1
 QM_SMALL_MAX, QM_TOPK_MAX, QM_DECODE_MAX_TOKENS = 8, 32, 8
+QM_NOALLOC_SCRATCH_BYTES = 32 << 20
 QM_PATH_AUTO, QM_PATH_DECODE, QM_PATH_PREFILL = 0, 1, 2
 
 EXPORTS = ("qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
-           "moe_gate_up", "moe_down", "qm_strerror")
+           "moe_gate_up", "moe_down", "moe_expert_ffn_noalloc", "qm_strerror")
 
 
 class QmError(RuntimeError):
@@ -65,6 +66,8 @@ def load(path=LIB_PATH):
     L.moe_gate_up.restype = ctypes.c_int
     L.moe_down.argtypes = [ctypes.POINTER(Experts), vp, i32, vp, vp, i32, vp, vp, sz, vp]
     L.moe_down.restype = ctypes.c_int
+    L.moe_expert_ffn_noalloc.argtypes = [ctypes.POINTER(Experts), vp, i32, i32, vp, vp, i32, vp, vp]
+    L.moe_expert_ffn_noalloc.restype = ctypes.c_int
     L.qm_strerror.argtypes = [ctypes.c_int]
     L.qm_strerror.restype = ctypes.c_char_p
     return L
@@ -146,6 +149,14 @@ def moe_expert_ffn(ex, x, topk_ids, topk_w, y, workspace, stream=None, path=QM_P
     _check(lib.moe_expert_ffn_path(ctypes.byref(ex), _ptr(x), _dtype_code(x), T, _ptr(topk_ids), _ptr(topk_w), k,
                                    _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream), path))
+    return y
+
+
+def moe_expert_ffn_noalloc(ex, x, topk_ids, topk_w, y, stream=None):
+    """moe_expert_ffn on the library's fixed per-GPU scratch (no workspace)."""
+    T, k = topk_ids.shape
+    _check(lib.moe_expert_ffn_noalloc(ctypes.byref(ex), _ptr(x), _dtype_code(x), T, _ptr(topk_ids), _ptr(topk_w), k,
+                                      _ptr(y), _stream(stream)))
     return y
 
 

@@ -34,7 +34,8 @@ def q():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     assert set(names) == {"qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
-                          "moe_expert_ffn_path", "moe_gate_up", "moe_down", "qm_strerror"}
+                          "moe_expert_ffn_path", "moe_gate_up", "moe_down", "moe_expert_ffn_noalloc",
+                          "qm_strerror"}
 
 
 def test_library_exports_every_declared_symbol(q):
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_strerror(q):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert q.lib.qm_strerror(st)
     assert q.lib.qm_strerror(12345) == b"unknown status"
 
@@ -209,3 +210,24 @@ def test_workspace_sizes(q):
         q.lib.moe_expert_ffn_workspace(ctypes.byref(ex8), 8, 8)
     assert q.lib.moe_expert_ffn_workspace(ctypes.byref(ex), 1, 0) == 0
     assert q.lib.moe_expert_ffn_workspace(None, 1, 8) == 0
+
+
+def _moe_noalloc(q, ex, T=1, k=8, x=FAKE, dt=1):
+    f = ctypes.c_void_p(FAKE)
+    return q.raw_status("moe_expert_ffn_noalloc", ctypes.byref(ex), ctypes.c_void_p(x), dt, T, f, f, k, f, None)
+
+
+def test_moe_noalloc_rejects_before_any_hip_call(q):
+    """Malformed calls and calls needing more than the fixed scratch are
+    refused on the host, before the scratch address is looked up."""
+    assert _moe_noalloc(q, _experts(q), dt=5) == -1
+    assert _moe_noalloc(q, _experts(q), k=0) == -1
+    assert _moe_noalloc(q, _experts(q), x=0) == -1
+    assert _moe_noalloc(q, _experts(q, E=0)) == -1
+    assert _moe_noalloc(q, _experts(q), k=33) == -2
+    assert _moe_noalloc(q, _experts(q), T=0, x=0) == 0
+    big = _experts(q, E=256, H=6144, I=2048)
+    need = q.lib.moe_expert_ffn_workspace(ctypes.byref(big), 512, 8)
+    assert need > q.QM_NOALLOC_SCRATCH_BYTES
+    assert _moe_noalloc(q, big, T=512) == q.QM_ERR_TOO_LARGE
+    assert b"scratch" in q.lib.qm_strerror(q.QM_ERR_TOO_LARGE)
