@@ -19,11 +19,11 @@
  *  - Pointers marked "device" are HIP device pointers; the caller owns every
  *    buffer (weights, activations, outputs, workspace).  The library keeps no
  *    pointer after a call returns and allocates nothing.  Its only global
- *    state is a thread-safe call counter (the nonce of the one-launch decode
- *    layer's tile flags) and a per-device occupancy figure cached on first
- *    use, so calls are reentrant.  Two calls must not share one workspace
- *    while both are in flight (on different streams), as for any scratch
- *    buffer.
+ *    state is, per device, the compute-unit count (looked up once, kept in
+ *    an atomic) and the address of moe_expert_ffn_noalloc's scratch array
+ *    (looked up once under a mutex), so calls are reentrant.  Two calls must
+ *    not share one workspace while both are in flight (on different
+ *    streams), as for any scratch buffer.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls only enqueue work and return; results are ready when the stream
  *    reaches them.  Time them with events on that stream.
@@ -52,14 +52,20 @@
  *    Rows are ceil(k/64) * 24 bytes (a ragged last group is padded).
  *    group_size must be 64.  qgemv, qgemv_pair and qgemm_small with batch 1
  *    take it (k <= 16384); the expert FFN does not (QM_ERR_UNSUPPORTED).
- *  Value = element * its scale.  Accumulation on the GPU is fp32.
- *  Single-token int4 and int8 calls (qgemv, qgemv_pair, the one-token
- *  expert FFN: the shapes listed with each entry point's fast path) take
- *  integer dot products: each group of 16 consecutive activations (x, and the
- *  expert FFN's hidden vector) is scaled by a power of two and rounded to
- *  integers of at most 15 bits, so an activation is off by at most
- *  2^-15 * 1.072 * (largest |activation| of its group); small-integer
- *  activations are exact.  Non-finite activations are not supported there.
+ *  Value = element * its scale.
+ *
+ * Arithmetic.  The int4 and int8 kernels apply the weights with integer dot
+ * products (eight int4 or four int8 products per instruction) to activations
+ * written as stacked 15-bit integer "digit planes": each group of 32 (int4) or
+ * 16 (int8) activations shares a power-of-two exponent, and a call uses as
+ * many planes as its widest group needs so that every activation is exact
+ * (bf16 input) or within 2^-15 of itself (fp32 input, and the expert FFN's
+ * fp32 hidden vector, in groups of 16).  The error of an output is therefore
+ * at most 2^-15 * sum_k |w_k x_k| plus fp32 accumulation, for any finite
+ * input: a large activation beside small ones costs more planes (more
+ * work), not accuracy.  Typical activations need two planes.  The int3
+ * GEMV (QM_FMT_INT3) and the prefill kernels (bf16 MFMA) use floating-point
+ * products instead (see their entry points).
  *
  * Shape limits of the GPU path (QM_ERR_UNSUPPORTED otherwise): int4 needs
  * k % 32 == 0, int8 needs k % 16 == 0; 1 <= k <= QM_K_MAX; q and x must be
@@ -126,16 +132,15 @@ typedef struct {
 
 /* y[r] = sum_c W[r][c] * x[c], r < w->n.
  * [V: qmatmul.comp note -- the dense quantized GEMV, one token]
- * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).
- * Fast path (integer dot products): int4 with k a multiple of 2048 up to
- * 16384, int8 per row with k a multiple of 1024 up to 16384.               */
+ * x: device, k elements of x_dtype.  y: device, n fp32 (overwritten).    */
 QM_API int qgemv(const qm_qmat *w, const void *x, int32_t x_dtype, float *y, void *stream);
 
 /* Two projections of one x: y1 = W1 x and y2 = W2 x (W1, W2 with the same k).
  * [V: PR summary, dense tier -- the two attention-input projections of one
- * x share a submission (the matmul_pair path)]  With the same format and group size and a bf16 x both
- * run in one launch (x staged once per workgroup, one dispatch instead of
- * two); otherwise as two launches on the stream.  x: device, k elements.
+ * x share a submission (the matmul_pair path)]  With the same format and
+ * grouping (int4 or int8) both run in one launch (x staged once per
+ * workgroup); otherwise as two launches on the stream.  x: device, k
+ * elements.
  * y1, y2: device, w1->n and w2->n fp32 (overwritten, must not overlap).
  * Both matrices are validated before anything is enqueued.                  */
 QM_API int qgemv_pair(const qm_qmat *w1, const qm_qmat *w2, const void *x, int32_t x_dtype, float *y1, float *y2,
@@ -156,7 +161,8 @@ QM_API int qgemv_norm_chain(const qm_qmat *w_a, const qm_qmat *w_kv, const float
                             void *stream);
 
 /* Y[t][r] = sum_c W[r][c] * X[t][c] for t < batch, reading W once for all
- * t.  [V: qmatmul.comp note -- the S-token batch of the same GEMV]
+ * t (int4 and int8; int3 takes batch 1 only).
+ * [V: qmatmul.comp note -- the S-token batch of the same GEMV]
  * x: device [batch][ldx] (ldx >= k, ldx*elemsize a multiple of 16 bytes).
  * y: device [batch][ldy] fp32 (ldy >= n).  1 <= batch <= QM_SMALL_MAX.     */
 QM_API int qgemm_small(const qm_qmat *w, const void *x, int32_t x_dtype, int32_t batch, int64_t ldx,
@@ -172,8 +178,12 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  *   y_t = sum_j topk_w[t][j] * (D_e h),  summed in slot order.
  * [V: qmatmul_gate_up.comp note and the K-expert group note; Q: weighted
  *  accumulation of the expert outputs; silu(z) = z / (1 + e^-z)]
- * Gate weights are used as given (no renormalisation).  Each routed
- * expert's weights are read once per call for all tokens routed to it.
+ * Gate weights are used as given (no renormalisation).  Decode: within one
+ * pass of tokens (all of a decode batch whose activations fit the kernels'
+ * LDS: up to 8 tokens at hidden 4608, 5 at 6144) each routed expert's gate
+ * and up rows are read once for all tokens routed to it, and its down rows
+ * are streamed by adjacent waves so that the second token's read hits the
+ * cache.
  * Ids outside [0, n_experts) are skipped (the pair contributes nothing);
  * the same id twice in one token is summed.
  * x:         device [n_tokens][hidden] of x_dtype (16-byte aligned rows)
@@ -182,19 +192,21 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  * workspace: device, >= moe_expert_ffn_workspace(ex, n_tokens, top_k) bytes,
  *            256-byte aligned; its contents are scratch (not preserved).
  * n_tokens <= QM_DECODE_MAX_TOKENS runs the decode kernels (fp32 hidden
- * vector); larger batches run the expert-grouped prefill kernels (bf16 MFMA,
- * hidden vector and fp32 activations rounded to bf16) when the experts
- * qualify -- int4 with a group size (or, per row, a row length) that is a
- * multiple of 64, at most 96 groups per row
- * (a multiple of 4, with 16-byte aligned scale arrays), hidden % 512 == 0,
- * inter % 256 == 0, n_experts <= 8192 -- and otherwise the decode kernels
- * QM_DECODE_MAX_TOKENS tokens at a time.                                   */
+ * vector as digit planes) in passes of as many tokens as fit their LDS;
+ * larger batches run the expert-grouped prefill kernels (bf16 MFMA, hidden
+ * vector and fp32 activations rounded to bf16) when the experts qualify --
+ * int4 with a group size (or, per row, a row length) that is a multiple of
+ * 64, at most 96 groups per row (a multiple of 4, with 16-byte aligned scale
+ * arrays), hidden % 512 == 0, inter % 256 == 0, n_experts <= 8192 -- and
+ * otherwise the decode kernels pass by pass.  The decode kernels take
+ * hidden up to 16384 (int4; 8192 int8) and inter up to 4096 (int4; 2048
+ * int8); other shapes return QM_ERR_UNSUPPORTED.                           */
 QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
                    const int32_t *topk_ids, const float *topk_w, int32_t top_k,
                    float *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_expert_ffn with the kernel path chosen by the caller: QM_PATH_AUTO,
- * QM_PATH_DECODE (any n_tokens, QM_DECODE_MAX_TOKENS per pass) or
+ * QM_PATH_DECODE (any n_tokens, in passes of a few tokens) or
  * QM_PATH_PREFILL (any n_tokens; QM_ERR_UNSUPPORTED for experts the
  * prefill kernels do not take, see moe_expert_ffn).                        */
 QM_API int moe_expert_ffn_path(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
@@ -205,10 +217,14 @@ QM_API int moe_expert_ffn_path(const qm_experts *ex, const void *x, int32_t x_dt
 /* Stage 1 of the decode path on its own (the fused gate+up dispatch of the
  * "qmatmul_gate_up.comp" commit note [V]): for every pair p = t*top_k + j
  * with a valid id e, h[p][:] = silu(G_e x_t) * (U_e x_t).  Rows of pairs with
- * an invalid id are not written.  Needs n_tokens <= QM_DECODE_MAX_TOKENS.
- * h: device fp32 [n_tokens*top_k][inter], 4-byte aligned.                   */
+ * an invalid id are not written.  n_tokens must fit one decode pass (at most
+ * QM_DECODE_MAX_TOKENS, fewer for very wide hidden sizes; QM_ERR_UNSUPPORTED
+ * otherwise).  h: device fp32 [n_tokens*top_k][inter], 4-byte aligned.
+ * workspace as for moe_expert_ffn (scratch for activations that need more
+ * than two digit planes).                                                   */
 QM_API int moe_gate_up(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
-                       const int32_t *topk_ids, int32_t top_k, float *h, void *stream);
+                       const int32_t *topk_ids, int32_t top_k, float *h, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* Stage 2 of the decode path on its own: y_t = sum_j topk_w[t][j] *
  * (D_e h[t*top_k + j]) in slot order, from the hidden rows that moe_gate_up

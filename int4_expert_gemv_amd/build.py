@@ -26,14 +26,13 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-# The sources the single-token decode kernels are built from (the fused
-# gate+up kernel whose counters the bench reports, and the down kernel).
-DECODE_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_t1_lds.hpp", "moe_t1_q.hpp", "moe_t1_s.hpp", "moe_t1_impl.hpp",
-                  "moe_decode_impl.hpp", "moe_decode.hip", "moe_decode_i4_bf16.hip", "qmoe.hip")
+# The sources the decode kernels are built from (the fused gate+up kernel
+# whose counters the bench reports, and the down kernel).
+DECODE_SOURCES = ("device.hpp", "launch.hpp", "planes.hpp", "moe_decode.hip", "qmoe.hip")
 
 
 # The sources of the prefill kernels.
-PREFILL_SOURCES = ("device.hpp", "launch.hpp", "lds_ring.hpp", "moe_prefill.hip", "qmoe.hip")
+PREFILL_SOURCES = ("device.hpp", "launch.hpp", "moe_prefill.hip", "qmoe.hip")
 
 
 def source_digest(names=None):

@@ -121,23 +121,9 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
     return e3 == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
   }
   const GemvArgs a = gemv_args(w, x, batch, ldx, y, ldy);
-  if (w->fmt == QM_FMT_INT4 && batch == 1) {
-    const hipError_t eq = launch_qgemv_q(xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a,
-                                         static_cast<hipStream_t>(stream));
-    if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
-  if (w->fmt == QM_FMT_INT4 && batch > 1) {
-    const hipError_t eq = launch_qgemv_qb(xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a,
-                                          static_cast<hipStream_t>(stream));
-    if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
-  if (w->fmt == QM_FMT_INT8_ROW && batch == 1) {
-    const hipError_t eq = launch_qgemv_q8(xdt, a, static_cast<hipStream_t>(stream));
-    if (eq != hipErrorNotSupported) return eq == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
-  const int NB = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
-  hipError_t err = launch_qgemv(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, NB,
-                                static_cast<hipStream_t>(stream));
+  const hipError_t err = launch_gemv_planes(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, nullptr,
+                                            static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
 
@@ -173,12 +159,6 @@ int check_experts(const qm_experts* ex) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-size_t decode_workspace(int T, int k, int H, int I) {
-  const size_t P = (size_t)T * k;
-  return align_up(P * I * 4, 256) + align_up(P * H * 4, 256) + align_up(P * I * 2, 256) + align_up(P * I / 4, 256) +
-         align_up(P * ((I + 15) / 16) * 8, 256);
-}
-
 ExpertArgs expert_args(const qm_experts* ex) {
   ExpertArgs e{};
   e.gq = static_cast<const uint8_t*>(ex->gate_q);
@@ -199,44 +179,27 @@ ExpertArgs expert_args(const qm_experts* ex) {
   return e;
 }
 
-// A value no earlier call has used (splitmix64 of a process-wide counter
-// seeded from the clock), never 0: the one-launch layer's tile flags take it,
-// so flags left in a workspace by earlier calls never read as set.
-uint64_t call_nonce() {
-  static std::atomic<uint64_t> ctr{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() *
-                                   0x9E3779B97F4A7C15ull};
-  uint64_t z = ctr.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  z ^= z >> 31;
-  return z ? z : 1;
+// Decode pass arguments for tokens [t0, t0 + nt) of a call.
+MoeDecArgs dec_args(const ExpertArgs& e, const void* x, int xdt, int t0, int nt, const int32_t* ids, const float* w,
+                    int k, float* h, float* y, void* ws) {
+  MoeDecArgs a{};
+  a.ex = e;
+  a.x = x ? static_cast<const char*>(x) + (size_t)t0 * e.H * xsize(xdt) : nullptr;
+  a.ids = ids + (size_t)t0 * k;
+  a.w = w ? w + (size_t)t0 * k : nullptr;
+  a.h = h ? h + (size_t)t0 * k * e.I : nullptr;
+  a.y = y ? y + (size_t)t0 * e.H : nullptr;
+  a.T = nt;
+  a.topk = k;
+  if (ws) moe_decode_ws_split(a, ws);
+  return a;
 }
 
-// Decode workspace: h [T*k][I] fp32, per-pair down outputs [T*k][H] fp32, h as
-// digit words [T*k][I/16][8] u32 and their factors [T*k][I/16] fp32, tile
-// flags [T*k][I/16] u64.
-MoeDecodeArgs decode_args(const ExpertArgs& e, const void* x, int T, const int32_t* ids, const float* w, int k,
-                          float* y, void* workspace) {
-  MoeDecodeArgs a{};
-  a.ex = e;
-  a.x = x;
-  a.ids = ids;
-  a.w = w;
-  char* ws = static_cast<char*>(workspace);
-  a.h = reinterpret_cast<float*>(ws);
-  if (ws) {
-    const size_t P = (size_t)T * k;
-    a.pout = reinterpret_cast<float*>(ws + align_up(P * e.I * 4, 256));
-    a.hq = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.pout) + align_up(P * e.H * 4, 256));
-    a.hqs = reinterpret_cast<float*>(reinterpret_cast<char*>(a.hq) + align_up(P * e.I * 2, 256));
-    a.flags = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.hqs) + align_up(P * e.I / 4, 256));
-    a.nonce = call_nonce();
-  }
-  a.y = y;
-  a.T = T;
-  a.topk = k;
-  a.rounds = 1;
-  return a;
+// tokens per decode pass for these experts (0: the decode kernels do not take them)
+int dec_tokens(const qm_experts* ex, int top_k) {
+  const ExpertArgs e = expert_args(ex);
+  const int t = moe_decode_tokens_per_pass(ex->fmt, top_k, e);
+  return (t >= 1 && moe_decode_supported(ex->fmt, t, top_k, e)) ? t : 0;
 }
 
 // grouped iff both projections' reduction lengths are split into groups
@@ -303,21 +266,10 @@ int qgemv_pair(const qm_qmat* w1, const qm_qmat* w2, const void* x, int32_t x_dt
     return r != QM_OK ? r : run_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n, stream);
   }
   const int g1 = eff_gs(w1->fmt, w1->group_size, w1->k), g2 = eff_gs(w2->fmt, w2->group_size, w2->k);
-  if (w1->fmt == QM_FMT_INT4 && w2->fmt == QM_FMT_INT4 && (g1 != 0) == (g2 != 0)) {
-    const hipError_t eq = launch_qgemv_q_pair(x_dtype, g1 != 0, gemv_args(w1, x, 1, w1->k, y1, w1->n),
-                                              gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
-    if (eq == hipSuccess) return QM_OK;
-    if (eq != hipErrorNotSupported) return QM_ERR_LAUNCH;
-  }
-  if (w1->fmt == QM_FMT_INT8_ROW && w2->fmt == QM_FMT_INT8_ROW) {
-    const hipError_t eq = launch_qgemv_q8_pair(x_dtype, gemv_args(w1, x, 1, w1->k, y1, w1->n),
-                                               gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
-    if (eq == hipSuccess) return QM_OK;
-    if (eq != hipErrorNotSupported) return QM_ERR_LAUNCH;
-  }
-  if (w1->fmt == w2->fmt && g1 == g2) {
-    const hipError_t err = launch_qgemv_pair(w1->fmt, x_dtype, g1 != 0, gemv_args(w1, x, 1, w1->k, y1, w1->n),
-                                             gemv_args(w2, x, 1, w2->k, y2, w2->n), static_cast<hipStream_t>(stream));
+  if (w1->fmt == w2->fmt && (g1 != 0) == (g2 != 0) && w1->fmt != QM_FMT_INT3) {
+    // one launch: x staged once per workgroup for both matrices
+    const GemvArgs a1 = gemv_args(w1, x, 1, w1->k, y1, w1->n), a2 = gemv_args(w2, x, 1, w2->k, y2, w2->n);
+    const hipError_t err = launch_gemv_planes(w1->fmt, x_dtype, g1 != 0, a1, &a2, static_cast<hipStream_t>(stream));
     if (err == hipSuccess) return QM_OK;
     if (err != hipErrorNotSupported) return QM_ERR_LAUNCH;
   }
@@ -347,9 +299,13 @@ int qgemm_small(const qm_qmat* w, const void* x, int32_t x_dtype, int32_t batch,
 size_t moe_expert_ffn_workspace(const qm_experts* ex, int32_t n_tokens, int32_t top_k) {
   if (!ex || n_tokens < 0 || top_k < 1 || top_k > QM_TOPK_MAX) return 0;
   if (ex->hidden < 1 || ex->inter < 1 || ex->n_experts < 1) return 0;
-  const int td = n_tokens < QM_DECODE_MAX_TOKENS ? n_tokens : QM_DECODE_MAX_TOKENS;
-  size_t need = decode_workspace(td, top_k, ex->hidden, ex->inter);
+  size_t need = 0;
   if (moe_shape_ok(ex)) {
+    const int tpp = dec_tokens(ex, top_k);
+    if (tpp > 0) {
+      const int td = n_tokens < tpp ? n_tokens : tpp;
+      need = moe_decode_ws_bytes(td > 0 ? td : 1, top_k, ex->hidden, ex->inter);
+    }
     const ExpertArgs e = expert_args(ex);
     if (moe_prefill_supported(ex->fmt, top_k, e)) {
       const size_t p = moe_prefill_workspace(n_tokens, top_k, e);
@@ -375,9 +331,11 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
   const bool pre_ok = moe_prefill_supported(ex->fmt, top_k, expert_args(ex));
+  const int tpp = dec_tokens(ex, top_k);
   if (path == QM_PATH_AUTO)
-    path = (n_tokens > QM_DECODE_MAX_TOKENS && pre_ok) ? QM_PATH_PREFILL : QM_PATH_DECODE;
+    path = (n_tokens > QM_DECODE_MAX_TOKENS && pre_ok) || tpp == 0 ? QM_PATH_PREFILL : QM_PATH_DECODE;
   if (path == QM_PATH_PREFILL && !pre_ok) return QM_ERR_UNSUPPORTED;
+  if (path == QM_PATH_DECODE && tpp == 0) return QM_ERR_UNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) ||
       workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
@@ -388,26 +346,20 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
   if (path == QM_PATH_PREFILL) {
     err = launch_moe_prefill(ex->fmt, x_dtype, e, x, topk_ids, topk_w, n_tokens, top_k, y, workspace, s);
   } else {
-    // decode kernels, QM_DECODE_MAX_TOKENS tokens per pass (one pass for a decode batch)
-    const size_t xs = (size_t)ex->hidden * xsize(x_dtype);
-    for (int t0 = 0; t0 < n_tokens && err == hipSuccess; t0 += QM_DECODE_MAX_TOKENS) {
-      const int nt = n_tokens - t0 < QM_DECODE_MAX_TOKENS ? n_tokens - t0 : QM_DECODE_MAX_TOKENS;
-      MoeDecodeArgs a = decode_args(e, static_cast<const char*>(x) + (size_t)t0 * xs, nt,
-                                    topk_ids + (size_t)t0 * top_k, topk_w + (size_t)t0 * top_k, top_k,
-                                    y + (size_t)t0 * ex->hidden, workspace);
-      err = launch_moe_ffn_layer(ex->fmt, x_dtype, grouped, a, s);
-      if (err == hipErrorNotSupported) {
-        a.hq_ready = moe_gate_up_writes_digits(ex->fmt, a) ? 1 : 0;
-        err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, s);
-        if (err == hipSuccess) err = launch_moe_down(ex->fmt, grouped, a, s);
-      }
+    // decode kernels, up to tpp tokens per pass (one pass for a decode batch
+    // whose activations' digit planes fit the LDS)
+    for (int t0 = 0; t0 < n_tokens && err == hipSuccess; t0 += tpp) {
+      const int nt = n_tokens - t0 < tpp ? n_tokens - t0 : tpp;
+      const MoeDecArgs a = dec_args(e, x, x_dtype, t0, nt, topk_ids, topk_w, top_k, nullptr, y, workspace);
+      err = launch_moe_gate_up2(ex->fmt, x_dtype, grouped, a, s);
+      if (err == hipSuccess) err = launch_moe_down2(ex->fmt, grouped, a, false, s);
     }
   }
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
 int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_ids,
-                int32_t top_k, float* h, void* stream) {
+                int32_t top_k, float* h, void* workspace, size_t workspace_bytes, void* stream) {
   if (x_dtype != QM_F32 && x_dtype != QM_BF16) return QM_ERR_INVALID;
   if (n_tokens < 0 || top_k < 1) return QM_ERR_INVALID;
   int st = check_experts(ex);
@@ -415,14 +367,19 @@ int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_
   if (n_tokens == 0) return QM_OK;
   if (!x || !topk_ids || !h) return QM_ERR_INVALID;
   if (st != QM_OK) return st;
-  if (top_k > QM_TOPK_MAX || n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
+  if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(h, 4) || !aligned(topk_ids, 4)) return QM_ERR_UNSUPPORTED;
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
-  MoeDecodeArgs a = decode_args(expert_args(ex), x, n_tokens, topk_ids, nullptr, top_k, nullptr, nullptr);
-  a.h = h;
-  hipError_t err = launch_moe_gate_up(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
+  const int tpp = dec_tokens(ex, top_k);
+  if (tpp == 0 || n_tokens > tpp) return QM_ERR_UNSUPPORTED;  // one decode pass
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+    return QM_ERR_WORKSPACE;
+  MoeDecArgs a = dec_args(expert_args(ex), x, x_dtype, 0, n_tokens, topk_ids, nullptr, top_k, h, nullptr, workspace);
+  a.hq = nullptr;  // h only: no digit planes for a down pass
+  const hipError_t err = launch_moe_gate_up2(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
 
@@ -434,16 +391,19 @@ int moe_down(const qm_experts* ex, const float* h, int32_t n_tokens, const int32
   if (n_tokens == 0) return QM_OK;
   if (!h || !topk_ids || !topk_w || !y) return QM_ERR_INVALID;
   if (st != QM_OK) return st;
-  if (top_k > QM_TOPK_MAX || n_tokens > QM_DECODE_MAX_TOKENS) return QM_ERR_UNSUPPORTED;
+  if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(h, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
+  const int tpp = dec_tokens(ex, top_k);
+  if (tpp == 0 || n_tokens > tpp) return QM_ERR_UNSUPPORTED;  // one decode pass
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
-  MoeDecodeArgs a = decode_args(expert_args(ex), nullptr, n_tokens, topk_ids, topk_w, top_k, y, workspace);
-  a.h = const_cast<float*>(h);
-  hipError_t err = launch_moe_down(ex->fmt, grouped, a, static_cast<hipStream_t>(stream));
+  const MoeDecArgs a = dec_args(expert_args(ex), nullptr, QM_F32, 0, n_tokens, topk_ids, topk_w, top_k,
+                                const_cast<float*>(h), y, workspace);
+  const hipError_t err = launch_moe_down2(ex->fmt, grouped, a, true, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
 

@@ -62,7 +62,7 @@ def load(path=LIB_PATH):
     L.moe_expert_ffn.restype = ctypes.c_int
     L.moe_expert_ffn_path.argtypes = [ctypes.POINTER(Experts), vp, i32, i32, vp, vp, i32, vp, vp, sz, vp, i32]
     L.moe_expert_ffn_path.restype = ctypes.c_int
-    L.moe_gate_up.argtypes = [ctypes.POINTER(Experts), vp, i32, i32, vp, i32, vp, vp]
+    L.moe_gate_up.argtypes = [ctypes.POINTER(Experts), vp, i32, i32, vp, i32, vp, vp, sz, vp]
     L.moe_gate_up.restype = ctypes.c_int
     L.moe_down.argtypes = [ctypes.POINTER(Experts), vp, i32, vp, vp, i32, vp, vp, sz, vp]
     L.moe_down.restype = ctypes.c_int
@@ -160,11 +160,11 @@ def moe_expert_ffn_noalloc(ex, x, topk_ids, topk_w, y, stream=None):
     return y
 
 
-def moe_gate_up(ex, x, topk_ids, h, stream=None):
+def moe_gate_up(ex, x, topk_ids, h, workspace, stream=None):
     """h: fp32 [T*k][inter] device tensor (stage 1 of the decode path)."""
     T, k = topk_ids.shape
     _check(lib.moe_gate_up(ctypes.byref(ex), _ptr(x), _dtype_code(x), T, _ptr(topk_ids), k, _ptr(h),
-                           _stream(stream)))
+                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return h
 
 

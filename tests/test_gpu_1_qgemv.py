@@ -152,8 +152,9 @@ def _wide_range_x(seed, k, xdt):
     (1, 512, 6144, 0, "bf16"), (1, 300, 16384, 0, "f32"), (1, 64, 2048, 0, "bf16"),
 ])
 def test_qgemv_one_token_wide_activation_range(q, oracle, fmt, n, k, gs, xdt):
-    """The integer-dot-product GEMV (one token, int4 k = 2048 m, int8 k = 1024 m)
-    within the bar for activations of very different magnitudes."""
+    """The GEMV on activation digit planes within the bar for activations of
+    very different magnitudes (groups whose values span many binades need
+    more planes)."""
     print("qgemv wide-range fmt=%d n=%d k=%d gs=%d x=%s" % (fmt, n, k, gs, xdt), flush=True)
     g = np.random.default_rng([9, fmt, n, k])
     qw, s = synth.quant_matrix(g, fmt, n, k, gs)

@@ -143,8 +143,8 @@ def test_moe_one_token_wide_activation_range(q, oracle, xdt):
 
 def test_moe_one_token_stages_match_layer(q):
     """moe_gate_up then moe_down (hidden vectors through the caller's buffer,
-    turned into digits by their own kernel) give the same y, bit for bit, as
-    moe_expert_ffn (digits written by the gate+up kernel itself)."""
+    turned into digit planes by their own kernel) give the same y, bit for
+    bit, as moe_expert_ffn (planes written by the gate+up kernel itself)."""
     E, H, I, T, k = 24, 6144, 2048, 1, 8
     ids, w = _routing(14, T, E, k)
     ex = synth.expert_set(14, 4, E, H, I, 64, experts=np.unique(ids))
@@ -157,20 +157,20 @@ def test_moe_one_token_stages_match_layer(q):
     h = torch.empty((T * k, I), dtype=torch.float32, device="cuda")
     xd, idd, wd = dev(x), dev(ids), dev(w)
     q.moe_expert_ffn(e, xd, idd, wd, y1, ws)
-    q.moe_gate_up(e, xd, idd, h)
+    q.moe_gate_up(e, xd, idd, h, ws)
     q.moe_down(e, h, idd, wd, y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
 
 
 @pytest.mark.parametrize("H,k,bad", [(2048, 8, False), (2048, 8, True), (2048, 4, False), (4096, 8, True)])
-def test_moe_small_experts_one_launch(q, oracle, H, k, bad):
-    """inter 512, one token: the one-launch layer (tile flags with a per-call
-    nonce), with fewer slots, invalid and duplicate ids, hidden 4096; two calls
-    on one workspace give identical y (the flags of the first never satisfy
-    the second)."""
+def test_moe_small_experts(q, oracle, H, k, bad):
+    """inter 512, one token (the small-expert decode layer), with fewer slots,
+    invalid and duplicate ids, hidden 4096; two calls on one workspace give
+    identical y (nothing the first call leaves in the workspace is read as
+    the second call's data)."""
     E, I, T = 24, 512, 1
-    print("moe one-launch H=%d k=%d bad=%s" % (H, k, bad), flush=True)
+    print("moe small experts H=%d k=%d bad=%s" % (H, k, bad), flush=True)
     ids, w = _routing(16 + H + k, T, E, k)
     if bad:
         ids[0, 1] = -1          # skipped
