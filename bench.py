@@ -183,7 +183,7 @@ def bench_moe(args, E, H, I):
     torch.cuda.synchronize()
     gs0.record()
     for j in range(args.steps):
-        qmoe.moe_gate_up(e, x_d[args.warmup + j], ids_d[args.warmup + j], h)
+        qmoe.moe_gate_up(e, x_d[args.warmup + j], ids_d[args.warmup + j], h, ws)
     gs1.record()
     torch.cuda.synchronize()
     gu_ms = gs0.elapsed_time(gs1) / args.steps
@@ -192,7 +192,7 @@ def bench_moe(args, E, H, I):
     # run them as one launch: then the two agree to fp32 rounding, not bit for bit)
     y2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
     last = n_steps - 1
-    qmoe.moe_gate_up(e, x_d[last], ids_d[last], h)
+    qmoe.moe_gate_up(e, x_d[last], ids_d[last], h, ws)
     qmoe.moe_down(e, h, ids_d[last], w_d[last], y2, ws)
     torch.cuda.synchronize()
     same = bool(torch.equal(y2, y[last]))

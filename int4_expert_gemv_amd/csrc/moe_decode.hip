@@ -40,7 +40,7 @@ constexpr int kGR = 1;          // intermediate rows per wave and gate+up unit
 constexpr int kGW = 16 / kGR;   // waves per workgroup (gate+up)
 constexpr int kGT = 64 * kGW;
 constexpr int kHT = 16;         // rows of the intermediate dimension per gate+up unit (one h group)
-constexpr int kMaxPairs = 256;  // (token, slot) pairs per launch: 8 tokens x top-k 32
+constexpr int kMaxPairs = 128;  // (token, slot) pairs per pass (passes are sized to fit)
 
 __device__ __forceinline__ int wuni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -56,16 +56,21 @@ struct Route {
   int uexp[kMaxPairs];          // expert id of unique u
   int ustart[kMaxPairs + 1];    // pairs of u: upair[ustart[u] .. ustart[u+1])
   int upair[kMaxPairs];
-  int tmp_id[kMaxPairs];        // scratch
+  int tmp_id[kMaxPairs];        // expert id of every pair (as given)
+  float wgt[kMaxPairs];         // routing weight of every pair (down only)
   int tmp_first[kMaxPairs];
   int tmp_rank[kMaxPairs];
   int tmp_u[kMaxPairs];
   int cnt[kMaxPairs];
 };
 
-__device__ void build_route(const int32_t* __restrict__ ids, int np, int E, Route& R) {
+__device__ void build_route(const int32_t* __restrict__ ids, int np, int E, Route& R,
+                            const float* __restrict__ w = nullptr) {
   const int tid = threadIdx.x;
-  if (tid < np) R.tmp_id[tid] = ids[tid];
+  if (tid < np) {
+    R.tmp_id[tid] = ids[tid];
+    if (w) R.wgt[tid] = w[tid];
+  }
   if (tid < kMaxPairs) R.cnt[tid] = 0;
   __syncthreads();
   if (tid < np) {
@@ -118,25 +123,22 @@ __device__ void build_route(const int32_t* __restrict__ ids, int np, int E, Rout
   __syncthreads();
 }
 
-// OR of v over aligned groups of G lanes (G = 4 or 8)
+// Reductions over aligned groups of G (4, 8 or 16) lanes with DPP row
+// operations; every lane of a group ends with the result.
 template <int G>
 __device__ __forceinline__ uint32_t group_or(uint32_t v) {
-  v |= (uint32_t)__shfl_xor((int)v, 1, 64);
-  v |= (uint32_t)__shfl_xor((int)v, 2, 64);
-  if constexpr (G >= 8) v |= (uint32_t)__shfl_xor((int)v, 4, 64);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+  if constexpr (G >= 8) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // other quad
   return v;
 }
-
-template <int G>
-__device__ __forceinline__ float group_max16(float v) {
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-template <int G>
-__device__ __forceinline__ float group_min16(float v) {
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+template <int G, bool MAX>
+__device__ __forceinline__ float group_minmax(float v) {
+  auto step = [&](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if constexpr (G >= 8) v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  if constexpr (G >= 16) v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
   return v;
 }
 
@@ -150,8 +152,8 @@ __device__ __forceinline__ void wave_h_planes(float v, uint32_t* __restrict__ hq
   const int lane = threadIdx.x & 63;
   const bool act = lane < 16;
   const float av = act ? fabsf(v) : 0.f;
-  const float amax = group_max16<16>(av);
-  const float amin = group_min16<16>(act && av > 0.f ? av : __builtin_huge_valf());
+  const float amax = group_minmax<16, true>(av);
+  const float amin = group_minmax<16, false>(act && av > 0.f ? av : __builtin_huge_valf());
   int E = 0, P = 1;
   if (amax > 0.f) {
     E = fexp(amax);
@@ -204,7 +206,12 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   constexpr int W = x_words<FMT>();
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ Route R;
-  __shared__ float h_tile[kMaxPairs][kHT];  // one unit's h, per pair of the unit
+  // h of the units in progress: kSlots units at a time, each slot counting
+  // the waves that have written their row (the last one turns the unit's h
+  // into digit planes) and the epilogues it has completed
+  constexpr int kSlots = 2;
+  __shared__ float h_tile[kSlots][kMaxPairs][kHT];
+  __shared__ int s_arrive[kSlots], s_done[kSlots];
   __shared__ int s_pmax;
   const ExpertArgs& ex = a.ex;
   const int H = ex.H, I = ex.I, T = a.T;
@@ -220,6 +227,10 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
 
   // x: group exponents and the plane count (largest over all tokens' groups)
   if (threadIdx.x == 0) s_pmax = 0;
+  if (threadIdx.x < kSlots) {
+    s_arrive[threadIdx.x] = 0;
+    s_done[threadIdx.x] = 0;
+  }
   int pneed = 1;
   for (int it = threadIdx.x; it < T * KCH; it += kGT) {
     const int t = it / KCH, c = it - t * KCH;
@@ -232,8 +243,8 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   const int P = block_max_int(pneed, &s_pmax);
 
   constexpr int NQ = 2 * kGR;  // weight rows per wave and unit: (gate, up) of each of its rows
-  u32x4 wa[NQ][CPL], wb[NQ][CPL];
-  float sa[NQ][CPL], sb[NQ][CPL];
+  u32x4 wa[NQ][CPL];
+  float sa[NQ][CPL];
   auto load_unit = [&](u32x4 (&wv)[NQ][CPL], float (&sv)[NQ][CPL], int unit) {
     const int u = unit / ntile, tile = unit - u * ntile;
     const int64_t e = R.uexp[u];
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   // every pair of the unit; last pass: h into h_tile (and a.h), else the
   // partial sums to a.ab
   auto compute_unit = [&](const u32x4 (&wv)[NQ][CPL], const float (&sv)[NQ][CPL], int unit, int p0, int np,
-                          bool last) {
+                          bool last, int slot) {
     const int u = unit / ntile, tile = unit - u * ntile;
     const int pb = R.ustart[u], pe = R.ustart[u + 1];
     for (int pi = pb; pi < pe; ++pi) {
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
           }
           if (last) {
             const float hv = silu(av) * bv;
-            h_tile[pi - pb][kGR * wave + hr] = hv;
+            h_tile[slot][pi - pb][kGR * wave + hr] = hv;
             if (a.h) a.h[(int64_t)pair * I + r] = hv;
           } else {
             abp[0] = av;
@@ -353,38 +364,39 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
       xf[t * KCH + c] = ldexpf(1.f, E - 14 - 15 * p0);
     }
     __syncthreads();
-    // DB: the next unit's weights load into the second buffer while one is
-    // computed (rows of one chunk per lane; longer rows load per unit)
-    constexpr bool DB = CPL == 1;
-    for (; unit < nunits; unit += (DB ? 2 : 1) * gridDim.x) {
-      const int u1 = unit + gridDim.x, u2 = unit + 2 * gridDim.x;
-      for (int half = 0; half < (DB ? 2 : 1); ++half) {
-        const int cur = half ? u1 : unit;
-        if (cur >= nunits) break;
-        const int nxt = half ? u2 : u1;
-        if (!DB) {
-          if (half == 0 && cur != (int)blockIdx.x) load_unit(wa, sa, cur);
-          compute_unit(wa, sa, cur, p0, np, last);
-        } else if (half == 0) {
-          if (nxt < nunits) load_unit(wb, sb, nxt);
-          compute_unit(wa, sa, cur, p0, np, last);
-        } else {
-          if (nxt < nunits) load_unit(wa, sa, nxt);
-          compute_unit(wb, sb, cur, p0, np, last);
-        }
-        if (!last || !a.hq) continue;  // h only (stage call): no digit planes
-        // the unit's h as digit planes, one wave per pair
-        __syncthreads();
-        const int uu = cur / ntile, tile = cur - uu * ntile;
-        const int pb = R.ustart[uu], pe = R.ustart[uu + 1];
-        for (int pi = pb + wave; pi < pe; pi += kGW) {
-          const int pair = R.upair[pi];
-          const int r = tile * kHT + lane;
-          const float hv = (lane < kHT && r < I) ? h_tile[pi - pb][lane] : 0.f;
-          const int64_t g = (int64_t)pair * ((I + 15) / 16) + tile;
-          wave_h_planes<FMT>(hv, a.hq + g * (kPlaneMax * 8), a.hf + g, a.hp + g);
-        }
-        __syncthreads();
+    // the next unit's weights are requested as soon as the current unit's
+    // registers are consumed; no workgroup barrier per unit: the last wave to
+    // write its row of a unit builds the unit's h digit planes, the others go
+    // on to their next unit
+    for (int j = 0; unit < nunits; unit += gridDim.x, ++j) {
+      const int cur = unit;
+      const int slot = j % kSlots;
+      const bool epi = last && a.hq;
+      if (epi && j >= kSlots) {
+        // the slot's previous unit must have had its epilogue
+        while (__hip_atomic_load(&s_done[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < j / kSlots)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      compute_unit(wa, sa, cur, p0, np, last, slot);
+      if (cur + (int)gridDim.x < nunits) load_unit(wa, sa, cur + gridDim.x);
+      if (!epi) continue;  // h only (stage call) or a partial pass: no digit planes
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(&s_arrive[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __shfl(old, 0, 64);
+      if (old != kGW - 1) continue;
+      // this wave wrote the unit's last row: digit planes of every pair's h
+      const int uu = cur / ntile, tile = cur - uu * ntile;
+      const int pb = R.ustart[uu], pe = R.ustart[uu + 1];
+      for (int pi = pb; pi < pe; ++pi) {
+        const int pair = R.upair[pi];
+        const int r = tile * kHT + lane;
+        const float hv = (lane < kHT && r < I) ? h_tile[slot][pi - pb][lane] : 0.f;
+        const int64_t g = (int64_t)pair * ((I + 15) / 16) + tile;
+        wave_h_planes<FMT>(hv, a.hq + g * (kPlaneMax * 8), a.hf + g, a.hp + g);
+      }
+      if (lane == 0) {
+        __hip_atomic_store(&s_arrive[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&s_done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   }
@@ -392,12 +404,14 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
 
 // ---- down + weighted combine -----------------------------------------------------
 // L lanes per down row (RW = 64 / L rows per wave pass); a lane holds CPL
-// chunk positions c = sub + L i of its pair's h digits (two planes).
-template <int FMT, bool GROUPED, int L, int CPL>
+// chunk positions c = sub + L i of its pair's h digits (two planes).  A wave
+// issues the loads of NB row passes (all of the workgroup's rows at the
+// shapes it is sized for) before it reads the pair's h digits, so the whole
+// row block is in flight at once.
+template <int FMT, bool GROUPED, int L, int CPL, int NB>
 __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
   constexpr int RW = 64 / L;
   constexpr int GPC = FMT == kFmtInt4 ? 2 : 1;  // h groups of 16 per chunk
-  constexpr int NR = CPL == 1 ? 4 : 2;          // row passes per load batch
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ Route R;
   const ExpertArgs& ex = a.ex;
@@ -409,13 +423,39 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
   const int sub = lane % L, rs = lane / L;
   const int Rb = (H + gridDim.x - 1) / gridDim.x;
   const int r0 = blockIdx.x * Rb, nr = min(Rb, H - r0);
+  const int npass = (nr + RW - 1) / RW;
   float* part = reinterpret_cast<float*>(lds);  // [Rb][np]
-  build_route(a.ids, np, ex.E, R);
+  build_route(a.ids, np, ex.E, R, a.w);
   const int nvalid = R.ustart[R.nu];
+
+  u32x4 wv[NB][CPL];
+  float sv[NB][CPL];
+  // the pair's expert's rows [r0, r0 + nr) as two buffer regions (weights,
+  // scales); byte offsets in vector registers
+  auto issue = [&](int e, int b0) {
+    const int64_t er0 = (int64_t)e * H + r0;
+    const __amdgpu_buffer_rsrc_t rq = region_rsrc(ex.dq + er0 * ex.rb_i, (uint32_t)(nr * ex.rb_i));
+    const __amdgpu_buffer_rsrc_t rsc = region_rsrc(ex.ds + er0 * ex.G_i, (uint32_t)(nr * ex.G_i * 4));
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int rl = min((b0 + j) * RW + rs, nr - 1);
+      const uint32_t qo = (uint32_t)(rl * ex.rb_i), so = (uint32_t)(rl * ex.G_i * 4);
+      if constexpr (!GROUPED) sv[j][0] = ld_region4(rsc, so);  // the row's one scale
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = sub + L * i;
+        if (b0 + j < npass && c < KCH) {
+          wv[j][i] = ld_region16(rq, qo + (uint32_t)c * 16);
+          if constexpr (GROUPED) sv[j][i] = ld_region4(rsc, so + (uint32_t)(c >> ex.gshift) * 4);
+        }
+      }
+    }
+  };
 
   for (int li = wave; li < nvalid; li += kMW) {
     const int pair = R.upair[li];
-    const int e = a.ids[pair];
+    const int e = R.tmp_id[pair];
+    issue(e, 0);
     // the pair's plane count over the groups this wave touches
     int pw = 1;
 #pragma unroll
@@ -442,10 +482,13 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
           hfac[i][gg] = c < KCH ? a.hf[g] * ldexpf(1.f, -15 * p0) : 0.f;
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
+            // read whether or not the group has this plane (its slot exists),
+            // then zero it: the loads do not wait for the plane count
             const bool on = p0 + pp < pg;
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.hq + g * (kPlaneMax * 8) + (p0 + pp) * 8);
-            const u32x4 q0 = on ? src[0] : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 q1 = on ? src[1] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.hq + g * (kPlaneMax * 8) + min(p0 + pp, kPlaneMax - 1) * 8);
+            const u32x4 r0 = src[0], r1 = src[1];
+            const u32x4 q0 = on ? r0 : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 q1 = on ? r1 : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               hd[pp][i][gg * 8 + k] = q0[k];
@@ -455,29 +498,10 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
         }
       }
       const int npl = min(2, pw - p0);
-      // rows of this workgroup, RW per pass, NR passes per batch of loads
-      const int npass = (nr + RW - 1) / RW;
-      for (int b0 = 0; b0 < npass; b0 += NR) {
-        u32x4 wv[NR][CPL];
-        float sv[NR][CPL];
+      for (int b0 = 0; b0 < npass; b0 += NB) {
+        if (b0 > 0 || p0 > 0) issue(e, b0);
 #pragma unroll
-        for (int j = 0; j < NR; ++j) {
-          const int rl = min((b0 + j) * RW + rs, nr - 1);
-          const int64_t er = (int64_t)e * H + r0 + rl;
-          const uint8_t* qrow = ex.dq + er * ex.rb_i;
-          const float* srow = ex.ds + er * ex.G_i;
-          if constexpr (!GROUPED) sv[j][0] = ld_stream(srow);  // the row's one scale
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const int c = sub + L * i;
-            if (b0 + j < npass && c < KCH) {
-              wv[j][i] = ld_stream(qrow + (int64_t)c * 16);
-              if constexpr (GROUPED) sv[j][i] = ld_stream(srow + (c >> ex.gshift));
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
+        for (int j = 0; j < NB; ++j) {
           if (b0 + j >= npass) break;
           float acc = 0.f;
 #pragma unroll
@@ -527,8 +551,7 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
     float v = 0.f;
     for (int j = 0; j < a.topk; ++j) {
       const int pair = t * a.topk + j;
-      const int id = a.ids[pair];
-      if (id >= 0 && id < ex.E) v = __builtin_fmaf(a.w[pair], part[(size_t)rl * np + pair], v);
+      if (R.tmp_first[pair] >= 0) v = __builtin_fmaf(R.wgt[pair], part[(size_t)rl * np + pair], v);
     }
     a.y[(int64_t)t * H + r0 + rl] = v;
   }
@@ -581,13 +604,24 @@ hipError_t launch_down(const MoeDecArgs& a, int cus, hipStream_t st) {
   const int blocks = (a.ex.H + Rb - 1) / Rb;    // every workgroup has rows
   const size_t lds = (size_t)Rb * a.T * a.topk * 4;
   if (lds > kDecLdsMax) return hipErrorNotSupported;
-#define QM_DN(L_, C)                                                                                     \
-  hipLaunchKernelGGL((moe_down_kernel<FMT, GROUPED, L_, C>), dim3(blocks), dim3(kMT), lds, st, a); \
+#define QM_DN(L_, C, NB_)                                                                                    \
+  hipLaunchKernelGGL((moe_down_kernel<FMT, GROUPED, L_, C, NB_>), dim3(blocks), dim3(kMT), lds, st, a); \
   return hipGetLastError();
-  if (KCH <= 16) { QM_DN(16, 1) }
-  if (KCH <= 32) { QM_DN(32, 1) }
-  if (KCH <= 64) { QM_DN(64, 1) }
-  if (KCH <= 128) { QM_DN(64, 2) }
+  // NB row passes in flight per wave: the whole row block when it fits
+  const int npass16 = (Rb + 3) / 4, npass32 = (Rb + 1) / 2;
+  if (KCH <= 16) {
+    if (npass16 <= 8) { QM_DN(16, 1, 8) }
+    QM_DN(16, 1, 16)
+  }
+  if (KCH <= 32) {
+    if (npass32 <= 12) { QM_DN(32, 1, 12) }
+    QM_DN(32, 1, 16)
+  }
+  if (KCH <= 64) {
+    if (Rb <= 12) { QM_DN(64, 1, 12) }
+    QM_DN(64, 1, 24)
+  }
+  if (KCH <= 128) { QM_DN(64, 2, 8) }
 #undef QM_DN
   return hipErrorNotSupported;
 }

@@ -131,26 +131,43 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 
 // Exact integer sum over one 16-byte chunk of int4 weights (w, each word
 // already XOR 0x88888888) against one plane of its 32-group (x[0..15]).
+// One independent chain per digit, combined at the end (the chains overlap
+// in the pipeline instead of each product waiting for the previous one).
 __device__ __forceinline__ int gdot_i4(const u32x4& w, const uint32_t* x) {
-  int t = sdot8(w[0], x[3], sdot8(w[1], x[7], sdot8(w[2], x[11], sdot8(w[3], x[15], 0))));
-  t = sdot8(w[0], x[2], sdot8(w[1], x[6], sdot8(w[2], x[10], sdot8(w[3], x[14], t << 4))));
-  t = sdot8(w[0], x[1], sdot8(w[1], x[5], sdot8(w[2], x[9], sdot8(w[3], x[13], t << 4))));
-  return sdot8(w[0], x[0], sdot8(w[1], x[4], sdot8(w[2], x[8], sdot8(w[3], x[12], t << 4))));
+  int t[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    t[d] = sdot8(w[0], x[d], sdot8(w[1], x[4 + d], sdot8(w[2], x[8 + d], sdot8(w[3], x[12 + d], 0))));
+  return (int)((uint32_t)t[0] + ((uint32_t)t[1] << 4) + ((uint32_t)t[2] << 8) + ((uint32_t)t[3] << 12));
 }
 
 // Exact integer sum over 16 int4 weights (words w0, w1, each XOR
 // 0x88888888) against one plane of their 16-group (x[0..7]: words 4j + d).
 __device__ __forceinline__ int gdot16_i4(uint32_t w0, uint32_t w1, const uint32_t* x) {
-  int t = sdot8(w0, x[3], sdot8(w1, x[7], 0));
-  t = sdot8(w0, x[2], sdot8(w1, x[6], t << 4));
-  t = sdot8(w0, x[1], sdot8(w1, x[5], t << 4));
-  return sdot8(w0, x[0], sdot8(w1, x[4], t << 4));
+  int t[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) t[d] = sdot8(w0, x[d], sdot8(w1, x[4 + d], 0));
+  return (int)((uint32_t)t[0] + ((uint32_t)t[1] << 4) + ((uint32_t)t[2] << 8) + ((uint32_t)t[3] << 12));
 }
 
 // The same for 16 int8 weights (words w[0..3]) against a 16-group's plane.
 __device__ __forceinline__ int gdot_i8(const u32x4& w, const uint32_t* x) {
   int t = sdot4(w[0], x[1], sdot4(w[1], x[3], sdot4(w[2], x[5], sdot4(w[3], x[7], 0))));
   return sdot4(w[0], x[0], sdot4(w[1], x[2], sdot4(w[2], x[4], sdot4(w[3], x[6], t << 8))));
+}
+
+// Streaming loads through a buffer resource: one descriptor (scalar
+// registers) for a whole region and per-lane byte offsets in vector
+// registers, so that many rows in flight do not each hold a 64-bit scalar
+// address.  Non-temporal (weights are read once per call).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld_region16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ float ld_region4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2));
 }
 
 // Load N (16 or 32) activations (bf16 or fp32) starting at element `e0` of `x`.
