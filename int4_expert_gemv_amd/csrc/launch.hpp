@@ -42,9 +42,7 @@ struct MoeDecArgs {
   float* h;            // optional fp32 h [T*k][I] (stage output / caller input)
   float* y;            // [T][H]
   int T, topk;
-  uint32_t* hq;        // workspace: h digit planes [T*k][I/16][kPlaneMax][8]
-  float* hf;           // workspace: their factors [T*k][I/16]
-  int* hp;             // workspace: their plane counts [T*k][I/16]
+  uint8_t* hrec;       // workspace: h records [T*k][kRecPairs][8 * ceil(I / 128)][96 B] (moe_decode.hip)
   float* ab;           // workspace: gate/up partial sums between passes [T*k][I][2]
 };
 

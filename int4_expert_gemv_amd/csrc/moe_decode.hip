@@ -27,6 +27,8 @@
 //     y_t = sum_j w_tj o_tj in slot order, so y does not depend on timing.
 // Activations needing more than two planes (very wide value ranges) are
 // consumed two planes per pass; weights are then read once per pass.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "planes.hpp"
 
@@ -36,7 +38,7 @@ namespace {
 
 constexpr int kMW = 8;          // waves per workgroup (down)
 constexpr int kMT = 64 * kMW;   // threads per workgroup (down)
-constexpr int kGR = 1;          // intermediate rows per wave and gate+up unit
+constexpr int kGR = 2;          // intermediate rows per wave and gate+up unit
 constexpr int kGW = 16 / kGR;   // waves per workgroup (gate+up)
 constexpr int kGT = 64 * kGW;
 constexpr int kHT = 16;         // rows of the intermediate dimension per gate+up unit (one h group)
@@ -64,12 +66,13 @@ struct Route {
   int cnt[kMaxPairs];
 };
 
-__device__ void build_route(const int32_t* __restrict__ ids, int np, int E, Route& R,
-                            const float* __restrict__ w = nullptr) {
+// (id, w: this thread's pair's expert id and routing weight, threads < np;
+// loaded by the caller, so that other loads can be in flight meanwhile)
+__device__ void build_route(int id_t, float w_t, int np, int E, Route& R) {
   const int tid = threadIdx.x;
   if (tid < np) {
-    R.tmp_id[tid] = ids[tid];
-    if (w) R.wgt[tid] = w[tid];
+    R.tmp_id[tid] = id_t;
+    R.wgt[tid] = w_t;
   }
   if (tid < kMaxPairs) R.cnt[tid] = 0;
   __syncthreads();
@@ -134,7 +137,7 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
 }
 template <int G, bool MAX>
 __device__ __forceinline__ float group_minmax(float v) {
-  auto step = [&](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  auto step = [&](float a, float b) __attribute__((always_inline)) { return MAX ? fmaxf(a, b) : fminf(a, b); };
   v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
   v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
   if constexpr (G >= 8) v = step(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
@@ -142,13 +145,73 @@ __device__ __forceinline__ float group_minmax(float v) {
   return v;
 }
 
-// Digit planes of 16 fp32 values held one per lane by lanes 0..15 of a wave
-// (lanes 16..63 pass anything, write nothing): factor 2^(E-14), plane count
-// and the planes' words, to hq[kPlaneMax][8].  Same encoding as planes.hpp
-// (fp32 rule for the plane count).  Called by a whole wave.
+// Sum over aligned groups of L (16, 32 or 64) lanes, complete in the
+// group's last lane (L - 1 of the group; other lanes hold partial sums):
+// rows of 16 lanes by DPP, then row broadcasts 15 and 31 carry row sums
+// into the following rows.
+template <int L>
+__device__ __forceinline__ float sum_to_last(float v) {
+  v = group_sum<16>(v);
+  if constexpr (L >= 32)  // row_bcast:15 into rows 1 and 3
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  if constexpr (L >= 64)  // row_bcast:31 into rows 2 and 3
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// ---- h records ---------------------------------------------------------------------
+// h (the intermediate activations) is taken in groups of 16 values (group G:
+// elements 16 G .. 16 G + 15) and turned into digit planes (planes.hpp
+// encoding, fp32 rule for the plane count P), written as records of two
+// planes each ("plane pair" q: planes 2q and 2q + 1), 96 bytes:
+//   bytes  0..63  for column c = 2 (plane - 2q) + b, 16 int8 digits: the
+//                 plane's value X split as X = lo + 256 hi (lo its signed low
+//                 byte; b = 0: lo, 1: hi); digit j is element dn_elem(j),
+//                 the order in which the down kernel unpacks weights;
+//   bytes 64..79  per column, int32: -8 x (sum of its digits) for int4
+//                 weights (the matrix instruction takes the nibbles u as
+//                 unsigned bytes, and sum (u - 8) d = sum u d - 8 sum d), 0
+//                 for int8 weights;
+//   bytes 80..83  the factor 2^(E - 14 - 30 q);
+//   bytes 84..87  the group's plane count P (bits 8 and up: free for the
+//                 down kernel's own use);
+// so that the group's sum_k w_k h_k is, exactly up to fp32 rounding,
+// factor x sum_c 2^(-15 p) 256^b (sum_j w_j d_cj + Cin_c) over its records.
+// A pair's records: plane pair q, group G at
+// hrec + ((pair * kRecPairs + q) * NGP + G) * kRecBytes, NGP = 8 ceil(I / 128)
+// (groups past I / 16 are never written and never read).
+constexpr int kRecBytes = 96;
+constexpr int kRecPairs = kPlaneMax / 2;
+
+__host__ __device__ constexpr int dn_ngp(int I) { return 8 * ((I + 127) / 128); }
+
+// element of digit j of a group's column (the weights' unpacking order: an
+// int4 word w gives bytes (w & 0x0F0F0F0F) = nibbles 0, 2, 4, 6 and
+// (w >> 4) & 0x0F0F0F0F = nibbles 1, 3, 5, 7)
 template <int FMT>
-__device__ __forceinline__ void wave_h_planes(float v, uint32_t* __restrict__ hq, float* __restrict__ hf,
-                                              int* __restrict__ hp) {
+__device__ __forceinline__ int dn_elem(int j) {
+  if constexpr (FMT == kFmtInt4) {
+    const int v = j >> 2, jj = j & 3;
+    return ((v & 2) ? 8 : 0) + 2 * jj + (v & 1);
+  } else {
+    return j;
+  }
+}
+
+__device__ __forceinline__ int group_isum16(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return v;
+}
+
+// The records of one group of 16 fp32 values held one per lane by lanes
+// 0..15 of a wave (lanes 16..63 pass anything, write nothing); rec: its plane
+// pair 0 record, qstride: bytes between its plane pairs' records.  At least
+// plane pair 0 is written (with zero digits past P).  Called by a whole wave.
+template <int FMT>
+__device__ __forceinline__ void wave_h_records(float v, uint8_t* __restrict__ rec, size_t qstride) {
   const int lane = threadIdx.x & 63;
   const bool act = lane < 16;
   const float av = act ? fabsf(v) : 0.f;
@@ -161,49 +224,59 @@ __device__ __forceinline__ void wave_h_planes(float v, uint32_t* __restrict__ hq
     P = span <= 0 ? 1 : min(kPlaneMax, 1 + (span + 14) / 15);
   }
   float r = act ? ldexpf(v, 14 - E) : 0.f;
-  for (int p = 0; p < P; ++p) {
-    const float X = __builtin_rintf(r);
-    r = (r - X) * 32768.f;
-    const int xi = (int)X;
-    uint32_t word[4];
-    if constexpr (FMT == kFmtInt4) {
-      // word (j, d) collects digit d of elements 8j .. 8j+7 as nibbles
-      const uint32_t U = (uint32_t)(xi + 0x8888);
+  const int nq = (P + 1) / 2;
+  const int t = lane & 15, c = t >> 2, vv = t & 3;  // this lane's output word: column c, word vv
+  for (int q = 0; q < nq; ++q) {
+    uint32_t packed = 0;  // the four column digits of this lane's element
 #pragma unroll
-      for (int d = 0; d < 4; ++d) word[d] = group_or<8>(((U >> (4 * d)) & 15u) << (4 * (lane & 7)));
-      if (act && (lane & 7) == 0) {
-        const int j = lane >> 3;
-        uint32_t* dst = hq + p * 8 + 4 * j;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) dst[d] = word[d] ^ 0x88888888u;
-      }
-    } else {
-      // word (k, 0) = low bytes, (k, 1) = high bytes of elements 4k .. 4k+3
+    for (int pp = 0; pp < 2; ++pp) {
+      const float X = __builtin_rintf(r);
+      r = (r - X) * 32768.f;
+      const int xi = (int)X;
       const int lo = (int)(int8_t)(uint8_t)(xi & 0xFF);
       const int hi = (xi - lo) >> 8;
-      word[0] = group_or<4>(((uint32_t)lo & 0xFFu) << (8 * (lane & 3)));
-      word[1] = group_or<4>(((uint32_t)hi & 0xFFu) << (8 * (lane & 3)));
-      if (act && (lane & 3) == 0) {
-        const int k = lane >> 2;
-        hq[p * 8 + 2 * k] = word[0];
-        hq[p * 8 + 2 * k + 1] = word[1];
-      }
+      packed |= (((uint32_t)lo & 0xFFu) << (16 * pp)) | (((uint32_t)hi & 0xFFu) << (16 * pp + 8));
     }
-  }
-  if (lane == 0) {
-    *hf = ldexpf(1.f, E - 14);
-    *hp = P;
+    if (!act) packed = 0u;
+    int sum[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) sum[cc] = group_isum16((int)(int8_t)(uint8_t)(packed >> (8 * cc)));
+    uint32_t word = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t src = (uint32_t)__shfl((int)packed, dn_elem<FMT>(4 * vv + jj), 64);
+      word |= ((src >> (8 * c)) & 0xFFu) << (8 * jj);
+    }
+    uint8_t* rq = rec + (size_t)q * qstride;
+    if (act) reinterpret_cast<uint32_t*>(rq)[t] = word;
+    if (lane == 0) {
+      int* ci = reinterpret_cast<int*>(rq + 64);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) ci[cc] = FMT == kFmtInt4 ? -8 * sum[cc] : 0;
+      *reinterpret_cast<float*>(rq + 80) = ldexpf(1.f, E - 14 - 30 * q);
+      *reinterpret_cast<int*>(rq + 84) = P;
+    }
   }
 }
 
 // ---- gate + up ---------------------------------------------------------------------
-// One 16-byte chunk of a gate or up row per lane and chunk position; wave w
-// of a unit takes intermediate rows 16 * tile + kGR w + (0 .. kGR-1): their
-// gate and up rows.
-template <int FMT, int XT, bool GROUPED, int CPL>
+// Wave w of a unit owns intermediate rows 16 * tile + kGR w + (0 .. kGR-1):
+// their gate and up rows (weight row q: row q / 2, gate for even q, up for
+// odd).  Lane l holds the 16-byte chunks c = l + 64 i (i < CPL) of each.
+// Every row is read through a buffer resource spanning exactly that row, so
+// chunks past its end (c >= KCH, or a row past I) load as zero without a
+// branch; in LDS those chunk positions hold zero digits and a zero factor.
+template <int CPL, bool GROUPED>
+struct GuRegs {
+  u32x4 w[2 * kGR][CPL];
+  float s[2 * kGR][GROUPED ? CPL : 1];
+};
+
+template <int FMT, int XT, bool GROUPED, int CPL, int NBUF>
 __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   constexpr int PER = per_chunk<FMT>();
   constexpr int W = x_words<FMT>();
+  constexpr int KCHP = 64 * CPL;  // chunk positions of an x row in LDS
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ Route R;
   // h of the units in progress: kSlots units at a time, each slot counting
@@ -216,81 +289,118 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   const ExpertArgs& ex = a.ex;
   const int H = ex.H, I = ex.I, T = a.T;
   const int KCH = H / PER;  // chunks per gate/up row
+  const int NGP = dn_ngp(I);
   const int wave = wuni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  uint32_t* xd = reinterpret_cast<uint32_t*>(lds);                          // [2][T][KCH][W]
-  float* xf = reinterpret_cast<float*>(lds + (size_t)2 * T * KCH * W * 4);  // [T][KCH]
+  uint32_t* xd = reinterpret_cast<uint32_t*>(lds);                           // [2][T][KCHP][W]
+  float* xf = reinterpret_cast<float*>(lds + (size_t)2 * T * KCHP * W * 4);  // [T][KCHP]
+  const size_t xps = (size_t)T * KCHP * W;                                   // words per plane
 
-  build_route(a.ids, T * a.topk, ex.E, R);
-  const int nu = R.nu;
-  const int ntile = (I + kHT - 1) / kHT;
-  const int nunits = nu * ntile;
-
-  // x: group exponents and the plane count (largest over all tokens' groups)
   if (threadIdx.x == 0) s_pmax = 0;
   if (threadIdx.x < kSlots) {
     s_arrive[threadIdx.x] = 0;
     s_done[threadIdx.x] = 0;
   }
-  int pneed = 1;
-  for (int it = threadIdx.x; it < T * KCH; it += kGT) {
-    const int t = it / KCH, c = it - t * KCH;
-    float v[PER];
-    load_acts<XT, PER>(a.x, (int64_t)t * H + (int64_t)c * PER, v);
-    int E;
-    pneed = max(pneed, group_planes<PER, XT>(v, &E));
-  }
-  __syncthreads();
-  const int P = block_max_int(pneed, &s_pmax);
-
-  constexpr int NQ = 2 * kGR;  // weight rows per wave and unit: (gate, up) of each of its rows
-  u32x4 wa[NQ][CPL];
-  float sa[NQ][CPL];
-  auto load_unit = [&](u32x4 (&wv)[NQ][CPL], float (&sv)[NQ][CPL], int unit) {
-    const int u = unit / ntile, tile = unit - u * ntile;
-    const int64_t e = R.uexp[u];
+  // the routing ids, then this thread's x groups (at most two: the launcher
+  // keeps T * KCHP <= twice the block size), requested together ahead of
+  // any weights (loads complete in order: staging x then waits for x alone)
+  const int id_t = threadIdx.x < T * a.topk ? a.ids[threadIdx.x] : -1;
+  constexpr int NV = XT == kBF16 ? PER / 8 : PER / 4;  // 16-byte words of a group
+  u32x4 raw[2][NV];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int r = min(tile * kHT + kGR * wave + (q >> 1), I - 1);
-      const int64_t er = e * I + r;
-      const uint8_t* qrow = ((q & 1) ? ex.uq : ex.gq) + er * ex.rb_h;
-      const float* srow = ((q & 1) ? ex.us : ex.gs) + er * ex.G_h;
-      if constexpr (!GROUPED) sv[q][0] = ld_stream(srow);  // the row's one scale
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int it = threadIdx.x + q2 * kGT;
+    const int t = min(it / KCHP, T - 1), c = it - (it / KCHP) * KCHP;
+    const bool real = it < T * KCHP && c < KCH;
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) +
+                                                      ((int64_t)t * H + (int64_t)(real ? c : 0) * PER) * (XT == kBF16 ? 2 : 4));
+#pragma unroll
+    for (int q = 0; q < NV; ++q) raw[q2][q] = src[q];
+  }
+  build_route(id_t, 0.f, T * a.topk, ex.E, R);
+  const int nu = R.nu;
+  const int ntile = (I + kHT - 1) / kHT;
+  const int nunits = nu * ntile;
+  const int G = gridDim.x;
+
+  // a unit's weights; a unit past the end (or a row past I) loads zeros
+  // without touching memory (empty buffer resources), so that callers issue
+  // loads unconditionally (no branch, hence exact wait counts after it)
+  auto load = [&](GuRegs<CPL, GROUPED>& g, int unit) __attribute__((always_inline)) {
+    const bool uok = unit < nunits;
+    const int uc = uok ? unit : 0;
+    const int u = uc / ntile, tile = uc - u * ntile;
+    const int64_t e = uok ? wuni(R.uexp[u]) : 0;
+#pragma unroll
+    for (int q = 0; q < 2 * kGR; ++q) {
+      const int r = tile * kHT + kGR * wave + (q >> 1);
+      const int64_t er = e * I + min(r, I - 1);
+      const bool ok = uok && r < I;
+      const __amdgpu_buffer_rsrc_t rq =
+          region_rsrc(((q & 1) ? ex.uq : ex.gq) + er * ex.rb_h, ok ? (uint32_t)ex.rb_h : 0u);
+      const __amdgpu_buffer_rsrc_t rs =
+          region_rsrc(((q & 1) ? ex.us : ex.gs) + er * ex.G_h, ok ? (uint32_t)ex.G_h * 4u : 0u);
+      if constexpr (!GROUPED) g.s[q][0] = ld_region4(rs, 0);  // the row's one scale
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        if (c < KCH) {
-          wv[q][i] = ld_stream(qrow + (int64_t)c * 16);
-          if constexpr (GROUPED) sv[q][i] = ld_stream(srow + (c >> ex.gshift));
-        }
+        const uint32_t c = (uint32_t)(lane + 64 * i);
+        g.w[q][i] = ld_region16(rq, c * 16u);
+        if constexpr (GROUPED) g.s[q][i] = ld_region4(rs, (c >> ex.gshift) * 4u);
       }
     }
+  };
+
+  // planes [p0, p0 + 2) of every token's x into LDS (zero past the row);
+  // returns the plane count this thread's groups need
+  auto stage = [&](int p0) __attribute__((always_inline)) {
+    int pneed = 1;
+    for (int it = threadIdx.x; it < T * KCHP; it += kGT) {
+      const int t = it / KCHP, c = it - t * KCHP;
+      uint32_t* dst = xd + ((size_t)t * KCHP + c) * W;
+      if (c < KCH) {
+        int E;
+        {
+          float v[PER];
+          load_acts<XT, PER>(a.x, (int64_t)t * H + (int64_t)c * PER, v);
+          pneed = max(pneed, group_planes<PER, XT>(v, &E));
+        }
+        stage_group<FMT, XT>(a.x, (int64_t)t * H + (int64_t)c * PER, E, p0, 2, dst, xps);
+        xf[t * KCHP + c] = ldexpf(1.f, E - 14 - 15 * p0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          dst[k] = 0u;
+          dst[xps + k] = 0u;
+        }
+        xf[t * KCHP + c] = 0.f;
+      }
+    }
+    return pneed;
   };
 
   // one unit against planes [p0, p0 + np) of x: a and b of the wave's row for
   // every pair of the unit; last pass: h into h_tile (and a.h), else the
   // partial sums to a.ab
-  auto compute_unit = [&](const u32x4 (&wv)[NQ][CPL], const float (&sv)[NQ][CPL], int unit, int p0, int np,
-                          bool last, int slot) {
+  auto compute = [&](const GuRegs<CPL, GROUPED>& g, int unit, int p0, int np, bool last, int slot)
+                     __attribute__((always_inline)) {
     const int u = unit / ntile, tile = unit - u * ntile;
-    const int pb = R.ustart[u], pe = R.ustart[u + 1];
+    const int pb = wuni(R.ustart[u]), pe = wuni(R.ustart[u + 1]);
     for (int pi = pb; pi < pe; ++pi) {
-      const int pair = R.upair[pi];
+      const int pair = wuni(R.upair[pi]);
       const int t = pair / a.topk;
-      float acc[NQ];
+      float acc[2 * kGR];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
+      for (int q = 0; q < 2 * kGR; ++q) acc[q] = 0.f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
-        if (c >= KCH) continue;
-        float ta[NQ];
+        float ta[2 * kGR];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) ta[q] = 0.f;
+        for (int q = 0; q < 2 * kGR; ++q) ta[q] = 0.f;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           if (pp >= np) break;
           const float ps = pp ? 1.f / 32768.f : 1.f;
-          const u32x4* src = reinterpret_cast<const u32x4*>(xd + ((size_t)(pp * T + t) * KCH + c) * W);
+          const u32x4* src = reinterpret_cast<const u32x4*>(xd + pp * xps + ((size_t)t * KCHP + c) * W);
           uint32_t xw[W];
 #pragma unroll
           for (int k4 = 0; k4 < W / 4; ++k4) {
@@ -301,31 +411,26 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
             xw[4 * k4 + 3] = v4[3];
           }
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            const int S = FMT == kFmtInt4 ? gdot_i4(wv[q][i] ^ 0x88888888u, xw) : gdot_i8(wv[q][i], xw);
+          for (int q = 0; q < 2 * kGR; ++q) {
+            const int S = FMT == kFmtInt4 ? gdot_i4(g.w[q][i] ^ 0x88888888u, xw) : gdot_i8(g.w[q][i], xw);
             ta[q] = __builtin_fmaf((float)S, ps, ta[q]);
           }
         }
-        const float f = xf[t * KCH + c];
+        const float f = xf[t * KCHP + c];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) acc[q] = __builtin_fmaf(ta[q], GROUPED ? f * sv[q][i] : f, acc[q]);
+        for (int q = 0; q < 2 * kGR; ++q) acc[q] = __builtin_fmaf(ta[q], GROUPED ? f * g.s[q][i] : f, acc[q]);
       }
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        acc[q] = group_sum<64>(acc[q]);
-        if (!GROUPED) acc[q] *= sv[q][0];  // the row's one scale
+      for (int q = 0; q < 2 * kGR; ++q) {
+        acc[q] = sum_to_last<64>(acc[q]);
+        if constexpr (!GROUPED) acc[q] *= g.s[q][0];  // the row's one scale
       }
-      if (lane < kGR) {  // lane hr finishes the wave's row hr
-        const int hr = lane;
-        const int r = tile * kHT + kGR * wave + hr;
-        float av = acc[0], bv = acc[1];
+      if (lane == 63) {  // the lane holding the sums
 #pragma unroll
-        for (int q = 1; q < kGR; ++q)
-          if (hr == q) {
-            av = acc[2 * q];
-            bv = acc[2 * q + 1];
-          }
-        if (r < I) {
+        for (int hr = 0; hr < kGR; ++hr) {
+          const int r = tile * kHT + kGR * wave + hr;
+          if (r >= I) continue;
+          float av = acc[2 * hr], bv = acc[2 * hr + 1];
           float* abp = a.ab + ((int64_t)pair * I + r) * 2;
           if (p0 > 0) {
             av += abp[0];
@@ -344,205 +449,553 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
     }
   };
 
-  for (int p0 = 0; p0 < P; p0 += 2) {
-    const int np = min(2, P - p0);
-    const bool last = p0 + 2 >= P;
-    int unit = blockIdx.x;
-    if (unit < nunits) load_unit(wa, sa, unit);  // first unit in flight during the staging
-    if (p0 > 0) __syncthreads();
-    // planes [p0, p0 + np) of every token's x
-    for (int it = threadIdx.x; it < T * KCH; it += kGT) {
-      const int t = it / KCH, c = it - t * KCH;
-      int E;
-      {
-        float v[PER];
-        load_acts<XT, PER>(a.x, (int64_t)t * H + (int64_t)c * PER, v);
-        group_planes<PER, XT>(v, &E);
-      }
-      stage_group<FMT, XT>(a.x, (int64_t)t * H + (int64_t)c * PER, E, p0, np, xd + ((size_t)t * KCH + c) * W,
-                           (size_t)T * KCH * W);
-      xf[t * KCH + c] = ldexpf(1.f, E - 14 - 15 * p0);
+  // after a unit's rows are written: the last wave to arrive turns the
+  // unit's h into digit planes (no workgroup barrier per unit)
+  auto epilogue = [&](int unit, int slot) __attribute__((always_inline)) {
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&s_arrive[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __shfl(old, 0, 64);
+    if (old != kGW - 1) return;
+    const int uu = unit / ntile, tile = unit - uu * ntile;
+    const int pb = wuni(R.ustart[uu]), pe = wuni(R.ustart[uu + 1]);
+    for (int pi = pb; pi < pe; ++pi) {
+      const int pair = wuni(R.upair[pi]);
+      const int r = tile * kHT + lane;
+      const float hv = (lane < kHT && r < I) ? h_tile[slot][pi - pb][lane] : 0.f;
+      wave_h_records<FMT>(hv, a.hrec + (((int64_t)pair * kRecPairs) * NGP + tile) * kRecBytes,
+                          (size_t)NGP * kRecBytes);
     }
-    __syncthreads();
-    // the next unit's weights are requested as soon as the current unit's
-    // registers are consumed; no workgroup barrier per unit: the last wave to
-    // write its row of a unit builds the unit's h digit planes, the others go
-    // on to their next unit
-    for (int j = 0; unit < nunits; unit += gridDim.x, ++j) {
-      const int cur = unit;
+    if (lane == 0) {
+      __hip_atomic_store(&s_arrive[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&s_done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  };
+
+  // all units of this workgroup against planes [p0, p0 + np) of x, weights
+  // of its first two units already requested into A and B
+  GuRegs<CPL, GROUPED> A, B;
+  auto run = [&](int p0, int np, bool last) __attribute__((always_inline)) {
+    const bool epi = last && a.hrec;
+    int unit = blockIdx.x, j = 0;
+    auto step = [&](GuRegs<CPL, GROUPED>& g) __attribute__((always_inline)) {
       const int slot = j % kSlots;
-      const bool epi = last && a.hq;
       if (epi && j >= kSlots) {
         // the slot's previous unit must have had its epilogue
         while (__hip_atomic_load(&s_done[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < j / kSlots)
           __builtin_amdgcn_s_sleep(1);
       }
-      compute_unit(wa, sa, cur, p0, np, last, slot);
-      if (cur + (int)gridDim.x < nunits) load_unit(wa, sa, cur + gridDim.x);
-      if (!epi) continue;  // h only (stage call) or a partial pass: no digit planes
-      int old = 0;
-      if (lane == 0) old = __hip_atomic_fetch_add(&s_arrive[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-      old = __shfl(old, 0, 64);
-      if (old != kGW - 1) continue;
-      // this wave wrote the unit's last row: digit planes of every pair's h
-      const int uu = cur / ntile, tile = cur - uu * ntile;
-      const int pb = R.ustart[uu], pe = R.ustart[uu + 1];
-      for (int pi = pb; pi < pe; ++pi) {
-        const int pair = R.upair[pi];
-        const int r = tile * kHT + lane;
-        const float hv = (lane < kHT && r < I) ? h_tile[slot][pi - pb][lane] : 0.f;
-        const int64_t g = (int64_t)pair * ((I + 15) / 16) + tile;
-        wave_h_planes<FMT>(hv, a.hq + g * (kPlaneMax * 8), a.hf + g, a.hp + g);
-      }
-      if (lane == 0) {
-        __hip_atomic_store(&s_arrive[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&s_done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
-  }
-}
-
-// ---- down + weighted combine -----------------------------------------------------
-// L lanes per down row (RW = 64 / L rows per wave pass); a lane holds CPL
-// chunk positions c = sub + L i of its pair's h digits (two planes).  A wave
-// issues the loads of NB row passes (all of the workgroup's rows at the
-// shapes it is sized for) before it reads the pair's h digits, so the whole
-// row block is in flight at once.
-template <int FMT, bool GROUPED, int L, int CPL, int NB>
-__global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
-  constexpr int RW = 64 / L;
-  constexpr int GPC = FMT == kFmtInt4 ? 2 : 1;  // h groups of 16 per chunk
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ Route R;
-  const ExpertArgs& ex = a.ex;
-  const int H = ex.H, I = ex.I;
-  const int np = a.T * a.topk;
-  const int KCH = I / per_chunk<FMT>();  // chunks per down row
-  const int NG = (I + 15) / 16;          // h groups per pair
-  const int wave = wuni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int sub = lane % L, rs = lane / L;
-  const int Rb = (H + gridDim.x - 1) / gridDim.x;
-  const int r0 = blockIdx.x * Rb, nr = min(Rb, H - r0);
-  const int npass = (nr + RW - 1) / RW;
-  float* part = reinterpret_cast<float*>(lds);  // [Rb][np]
-  build_route(a.ids, np, ex.E, R, a.w);
-  const int nvalid = R.ustart[R.nu];
-
-  u32x4 wv[NB][CPL];
-  float sv[NB][CPL];
-  // the pair's expert's rows [r0, r0 + nr) as two buffer regions (weights,
-  // scales); byte offsets in vector registers
-  auto issue = [&](int e, int b0) {
-    const int64_t er0 = (int64_t)e * H + r0;
-    const __amdgpu_buffer_rsrc_t rq = region_rsrc(ex.dq + er0 * ex.rb_i, (uint32_t)(nr * ex.rb_i));
-    const __amdgpu_buffer_rsrc_t rsc = region_rsrc(ex.ds + er0 * ex.G_i, (uint32_t)(nr * ex.G_i * 4));
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int rl = min((b0 + j) * RW + rs, nr - 1);
-      const uint32_t qo = (uint32_t)(rl * ex.rb_i), so = (uint32_t)(rl * ex.G_i * 4);
-      if constexpr (!GROUPED) sv[j][0] = ld_region4(rsc, so);  // the row's one scale
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = sub + L * i;
-        if (b0 + j < npass && c < KCH) {
-          wv[j][i] = ld_region16(rq, qo + (uint32_t)c * 16);
-          if constexpr (GROUPED) sv[j][i] = ld_region4(rsc, so + (uint32_t)(c >> ex.gshift) * 4);
-        }
+      compute(g, unit, p0, np, last, slot);
+      load(g, unit + NBUF * G);
+      if (epi) epilogue(unit, slot);
+      unit += G;
+      ++j;
+    };
+    while (unit < nunits) {
+      step(A);
+      if constexpr (NBUF == 2) {
+        if (unit >= nunits) break;
+        step(B);
       }
     }
   };
+  auto load_first = [&]() __attribute__((always_inline)) {
+    load(A, blockIdx.x);
+    if constexpr (NBUF == 2) load(B, blockIdx.x + G);
+  };
 
-  for (int li = wave; li < nvalid; li += kMW) {
-    const int pair = R.upair[li];
-    const int e = R.tmp_id[pair];
-    issue(e, 0);
-    // the pair's plane count over the groups this wave touches
-    int pw = 1;
+  int P;
+  {
+    const int unit = blockIdx.x;
+    load(A, unit);
+    int pneed = 1;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = sub + L * i;
-      if (c < KCH)
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int it = threadIdx.x + q2 * kGT;
+      if (it >= T * KCHP) break;
+      const int t = it / KCHP, c = it - t * KCHP;
+      uint32_t* dst = xd + ((size_t)t * KCHP + c) * W;
+      if (c < KCH) {
+        float xv[PER];
 #pragma unroll
-        for (int gg = 0; gg < GPC; ++gg) pw = max(pw, a.hp[(int64_t)pair * NG + c * GPC + gg]);
-    }
+        for (int q = 0; q < NV; ++q)
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) pw = max(pw, __shfl_xor(pw, o, 64));
-    pw = wuni(pw);
-    for (int p0 = 0; p0 < pw; p0 += 2) {
-      // h digits of planes p0, p0 + 1 (zero past a group's own plane count)
-      uint32_t hd[2][CPL][GPC * 8];
-      float hfac[CPL][GPC];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = sub + L * i;
-#pragma unroll
-        for (int gg = 0; gg < GPC; ++gg) {
-          const int64_t g = (int64_t)pair * NG + (c < KCH ? c * GPC + gg : 0);
-          const int pg = c < KCH ? a.hp[g] : 0;
-          hfac[i][gg] = c < KCH ? a.hf[g] * ldexpf(1.f, -15 * p0) : 0.f;
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            // read whether or not the group has this plane (its slot exists),
-            // then zero it: the loads do not wait for the plane count
-            const bool on = p0 + pp < pg;
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.hq + g * (kPlaneMax * 8) + min(p0 + pp, kPlaneMax - 1) * 8);
-            const u32x4 r0 = src[0], r1 = src[1];
-            const u32x4 q0 = on ? r0 : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 q1 = on ? r1 : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              hd[pp][i][gg * 8 + k] = q0[k];
-              hd[pp][i][gg * 8 + 4 + k] = q1[k];
-            }
-          }
-        }
-      }
-      const int npl = min(2, pw - p0);
-      for (int b0 = 0; b0 < npass; b0 += NB) {
-        if (b0 > 0 || p0 > 0) issue(e, b0);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if (b0 + j >= npass) break;
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const int c = sub + L * i;
-            if (c >= KCH) continue;
-            u32x4 w = wv[j][i];
-            float ta[GPC];
-#pragma unroll
-            for (int gg = 0; gg < GPC; ++gg) ta[gg] = 0.f;
-            if constexpr (FMT == kFmtInt4) {
-              w ^= 0x88888888u;
-#pragma unroll
-              for (int pp = 0; pp < 2; ++pp) {
-                if (pp >= npl) break;
-                const float ps = pp ? 1.f / 32768.f : 1.f;
-                ta[0] = __builtin_fmaf((float)gdot16_i4(w[0], w[1], hd[pp][i]), ps, ta[0]);
-                ta[GPC - 1] = __builtin_fmaf((float)gdot16_i4(w[2], w[3], hd[pp][i] + 8), ps, ta[GPC - 1]);
-              }
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (XT == kBF16) {
+              xv[8 * q + 2 * i] = __uint_as_float(raw[q2][q][i] << 16);
+              xv[8 * q + 2 * i + 1] = __uint_as_float(raw[q2][q][i] & 0xFFFF0000u);
             } else {
-#pragma unroll
-              for (int pp = 0; pp < 2; ++pp) {
-                if (pp >= npl) break;
-                const float ps = pp ? 1.f / 32768.f : 1.f;
-                ta[0] = __builtin_fmaf((float)gdot_i8(w, hd[pp][i]), ps, ta[0]);
-              }
+              xv[4 * q + i] = __uint_as_float(raw[q2][q][i]);
             }
-            float part_c = ta[0] * hfac[i][0];
-            if constexpr (GPC == 2) part_c = __builtin_fmaf(ta[1], hfac[i][1], part_c);
-            acc = __builtin_fmaf(part_c, GROUPED ? sv[j][i] : 1.f, acc);
           }
-          acc = group_sum<L>(acc);
-          const int rl = (b0 + j) * RW + rs;
-          if (sub == 0 && rl < nr) {
-            const float v = GROUPED ? acc : acc * sv[j][0];
-            float* dst = part + (size_t)rl * np + pair;
-            *dst = p0 == 0 ? v : *dst + v;
-          }
+        int E;
+        pneed = max(pneed, group_planes<PER, XT>(xv, &E));
+        stage_group_vals<FMT, PER>(xv, E, 0, dst, xps);
+        xf[t * KCHP + c] = ldexpf(1.f, E - 14);
+      } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          dst[k] = 0u;
+          dst[xps + k] = 0u;
+        }
+        xf[t * KCHP + c] = 0.f;
+      }
+    }
+    if constexpr (NBUF == 2) load(B, unit + G);
+    P = block_max_int(pneed, &s_pmax);  // (its barrier publishes the staging)
+  }
+  run(0, min(2, P), P <= 2);
+  // activations needing more planes (rare): planes two at a time, the
+  // partial sums carried in the workspace
+  for (int p0 = 2; p0 < P; p0 += 2) {
+    __syncthreads();  // the previous pass's LDS reads are done
+    stage(p0);
+    load_first();
+    __syncthreads();
+    run(p0, min(2, P - p0), p0 + 2 >= P);
+  }
+}
+
+// ---- down + weighted combine (matrix instructions) ------------------------------
+// y_t = sum_j w_tj D_e(tj) h_tj on v_mfma_i32_16x16x64_i8: C[m][n] = C_in[m][n]
+// + sum_k A[m][k] B[k][n] over 64 k, lane l holding row / column l % 16 and
+// k-slot l / 16 (16 bytes) of A and B, and C[4 (l / 16) + i][l % 16], i < 4.
+// B is 16 rows of D (a "tile"): lane (n, s) = (l % 16, l / 16) loads 16
+// bytes of row n, covering k in [128 kb2 + 32 s, +32) of the 128-wide k
+// block kb2 (int4: 32 nibbles; int8 weights: two loads), which feed the
+// k-slot s of two instructions ("steps" hh = 0, 1): in step hh, slot s is h
+// group G = 8 kb2 + 2 s + hh (16 k).  A row m = 4 g + c is column c of the
+// record of group 8 kb2 + 2 g + hh, zero outside slot g, so that every C
+// column sums over one group: one weight scale and one h factor.  Lane l's
+// four outputs are the columns of its own group (g = l / 16), the record's
+// Cin is the accumulator input, so each output is an exact integer, and
+//   o[n] += scale x factor x (C0 + 256 C1 + 2^-15 (C2 + 256 C3))
+// summed over the lane's k blocks and the four lanes of the row.
+//
+// A workgroup owns output rows [r0, r0 + nr) (tiles of 16).  A task is (a
+// routed pair, a tile); waves take the tasks in turn, their k blocks in
+// chunks of CK2, two chunks in flight per wave (registers A and B).  The
+// records (plane pair 0) of the pairs are staged in LDS, zero past the
+// pair's groups up to whole chunks; with one round for all pairs (the
+// usual case) a pair's LDS slot is its index and its records are requested
+// at the start with the routing ids, ahead of any weights.
+//
+// Groups with more than two planes: the thread that stages such a group's
+// record also requests its plane pair 1 record, gets a slot in item order
+// (a prefix count over the waves) and writes it there once its own weights
+// are requested; a step with such groups then adds that plane pair inside
+// its chunk.  Planes beyond those (and groups past the slots) are added
+// after the wave's chunks, reloading the few weights they need.
+// Per-(row, pair) results meet in LDS and every output is y_t = sum_j w_tj
+// o_tj in slot order, so y does not depend on timing.
+constexpr int kMaxTasks = 512;                  // tasks per round
+constexpr uint32_t kOutside = 0x80000000u;      // a buffer offset past every record: loads zeros
+constexpr size_t kDnLdsMax = 144 * 1024;        // dynamic LDS of the down kernel
+
+__host__ __device__ constexpr int dn_ck2(int fmt) { return fmt == kFmtInt4 ? 8 : 4; }
+// record slots per pair in LDS: whole chunks of k blocks
+__host__ __device__ constexpr int dn_ngl(int fmt, int I) {
+  return 8 * dn_ck2(fmt) * (((I + 127) / 128 + dn_ck2(fmt) - 1) / dn_ck2(fmt));
+}
+
+// SM: weight scales.  0: one per row; 1: per group (any size); 2: groups of 64.
+template <int FMT, int SM>
+__global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int xcap) {
+  constexpr int CK2 = dn_ck2(FMT);
+  constexpr int WV = FMT == kFmtInt4 ? 1 : 2;  // 16-byte weight loads per lane and k block
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ Route R;
+  __shared__ int s_task[kMaxTasks];
+  __shared__ int s_ntasks, s_xready, s_cnt[2][kMW];
+  const ExpertArgs& ex = a.ex;
+  const int H = ex.H, I = ex.I;
+  const int np = a.T * a.topk;
+  const int NK2 = (I + 127) / 128, NGP = dn_ngp(I), NG = (I + 15) / 16, NGL = dn_ngl(FMT, I);
+  const int CPT = (NK2 + CK2 - 1) / CK2;  // chunks per task
+  const int wave = wuni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, s = lane >> 4;
+  const int Rb = (H + gridDim.x - 1) / gridDim.x;
+  const int r0 = blockIdx.x * Rb, nr = min(Rb, H - r0);
+  const int ntile = (nr + 15) / 16;
+  float* part = reinterpret_cast<float*>(lds);                                             // [Rb][np]
+  uint8_t* rec = reinterpret_cast<uint8_t*>(lds + ((size_t)Rb * np * 4 + 15) / 16 * 16);  // [PR][NGL][96]
+  const uint8_t* zrec = rec + (size_t)PR * NGL * kRecBytes;                                // a zero record
+  uint8_t* xrec = const_cast<uint8_t*>(zrec) + kRecBytes;                                  // [xcap][96]
+  // the records of every pair: plane pairs q of pair p at (p kRecPairs + q) NGP
+  const uint32_t rec_bytes = (uint32_t)((size_t)np * kRecPairs * NGP * kRecBytes);
+  const __amdgpu_buffer_rsrc_t rall = region_rsrc(a.hrec, rec_bytes);
+
+  // staged items: (pair slot, group) records, 96 bytes (zero past I / 16)
+  const bool one = np <= PR;
+  u32x4 st[2][6];
+  auto stage_load = [&](int nit, int pb_, bool routed) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int it = min((int)threadIdx.x + kMT * j, max(nit, 1) - 1);
+      const int pr = it / NGL, g = it - pr * NGL;
+      const int pair = (one || !routed) ? pr : R.upair[pb_ + pr];
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(a.hrec + ((int64_t)pair * kRecPairs * NGP + min(g, NG - 1)) * kRecBytes);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) st[j][k] = src[k];
+    }
+  };
+  auto put = [&](int it, const u32x4* v6) __attribute__((always_inline)) {
+    const int g = it % NGL;
+    u32x4* dst = reinterpret_cast<u32x4*>(rec + (size_t)it * kRecBytes);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) dst[k] = g < NG ? v6[k] : u32x4{0u, 0u, 0u, 0u};
+  };
+  {
+    const int id_t = threadIdx.x < np ? a.ids[threadIdx.x] : -1;
+    const float w_t = threadIdx.x < np ? a.w[threadIdx.x] : 0.f;
+    stage_load(one ? np * NGL : 0, 0, false);
+    build_route(id_t, w_t, np, ex.E, R);
+  }
+  const int nu = R.nu, nvalid = R.ustart[nu];
+  if (threadIdx.x < kRecBytes / 4) reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(zrec))[threadIdx.x] = 0u;
+
+  struct Chunk {
+    u32x4 sc4[SM == 2 ? CK2 / 2 : 1];  // groups of 64: whole 16-byte loads
+    float sc[SM == 2 ? 1 : CK2];
+    u32x4 w[CK2][WV];
+  };
+  Chunk A, B;
+  float acc[4];
+  uint32_t xm0 = 0, xm1 = 0;  // the task's steps with further planes (bit 2 kb2 + hh)
+
+  int pb = 0, ub = 0;  // first pair and its unique expert of the round
+  while (pb < nvalid) {
+    // the round: pairs [pb, pe), ending at an expert boundary when one fits
+    int pe = min(nvalid, pb + PR);
+    int ue = ub;
+    while (ue < nu && R.ustart[ue + 1] <= pe) ++ue;  // experts wholly inside
+    if (ue > ub) pe = R.ustart[ue];
+    else ue = ub + 1;                                // one expert split over rounds
+    const int nit = one ? np * NGL : (pe - pb) * NGL;  // items staged for the round
+    auto slot_of = [&](int pi) __attribute__((always_inline)) { return one ? wuni(R.upair[pi]) : pi - pb; };
+    auto pair_of_slot = [&](int pr) __attribute__((always_inline)) { return one ? pr : R.upair[pb + pr]; };
+
+    __syncthreads();  // the previous round's LDS reads are done
+    if (threadIdx.x == 0) s_xready = 0;
+    if (!one) stage_load(nit, pb, true);
+    // the round's tasks: (place in the routing table, tile), packed
+    if (wave == 0) {
+      const int nt = (pe - pb) * ntile;
+      for (int i0 = 0; i0 < nt; i0 += 64) {
+        const int i = i0 + lane;
+        if (i < nt && i < kMaxTasks) s_task[i] = ((pb + i / ntile) << 12) | (i % ntile);
+      }
+      if (lane == 0) s_ntasks = min(nt, kMaxTasks);
+    }
+    // the thread's first two items: staged, and when they have more than two
+    // planes their plane pair 1 records requested (out of range: zeros)
+    u32x4 xr[2][6];
+    uint64_t xb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int it = threadIdx.x + kMT * j;
+      const int pr = it / NGL, g = it - pr * NGL;
+      const bool f = it < nit && g < NG && (int)(st[j][5][1] & 0xFFu) > 2;
+      xb[j] = __ballot(f);
+      const uint32_t off =
+          f ? (uint32_t)(((int64_t)pair_of_slot(f ? pr : 0) * kRecPairs + 1) * NGP + g) * kRecBytes : kOutside;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) xr[j][k] = __builtin_amdgcn_raw_buffer_load_b128(rall, off + 16u * k, 0, 0);
+      if (lane == 0) s_cnt[j][wave] = __popcll(xb[j]);
+      if (it < nit) put(it, st[j]);
+    }
+    for (int it = threadIdx.x + 2 * kMT; it < nit; it += kMT) {  // items past two per thread
+      const int pr = it / NGL, g = it - pr * NGL;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          a.hrec + ((int64_t)pair_of_slot(pr) * kRecPairs * NGP + min(g, NG - 1)) * kRecBytes);
+      u32x4 v6[6];
+#pragma unroll
+      for (int k = 0; k < 6; ++k) v6[k] = src[k];
+      put(it, v6);
+    }
+    __syncthreads();
+    const int ntasks = s_ntasks;
+    const int myt = wave < ntasks ? (ntasks - 1 - wave) / kMW + 1 : 0;  // this wave's tasks
+    const int nj = myt * CPT;                                            // and chunks
+    // slots of the thread's items with more planes: their rank in item order
+    int xslot[2];
+    {
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        for (int w = 0; w < kMW; ++w) base += (w < wave) ? s_cnt[j][w] : 0;
+        xslot[j] = base + __popcll(xb[j] & ((1ull << lane) - 1));
+        for (int w = wave; w < kMW; ++w) base += s_cnt[j][w];
+        if (((xb[j] >> lane) & 1) == 0 || xslot[j] >= xcap) xslot[j] = -1;
+        if (xslot[j] >= 0) {
+          int* pf = reinterpret_cast<int*>(rec + (size_t)(threadIdx.x + kMT * j) * kRecBytes + 84);
+          *pf = (*pf & 0xFF) | ((xslot[j] + 1) << 8);
         }
       }
     }
+
+    // chunk j of this wave: task wave + kMW (j / CPT), k blocks from
+    // CK2 (j % CPT); past the end: empty resources (loads of zeros)
+    auto task_rsrc = [&](bool ok, int tsk, __amdgpu_buffer_rsrc_t& rq, __amdgpu_buffer_rsrc_t& rsc)
+                         __attribute__((always_inline)) {
+      const int pi = tsk >> 12, tile = tsk & 0xFFF;
+      const int rows = min(16, nr - 16 * tile);
+      const int64_t er0 = (int64_t)(ok ? wuni(R.tmp_id[wuni(R.upair[pi])]) : 0) * H + r0 + 16 * tile;
+      rq = region_rsrc(ex.dq + er0 * ex.rb_i, ok ? (uint32_t)(rows * ex.rb_i) : 0u);
+      rsc = region_rsrc(ex.ds + er0 * ex.G_i, ok ? (uint32_t)(rows * ex.G_i * 4) : 0u);
+    };
+    auto wload = [&](__amdgpu_buffer_rsrc_t rq, uint32_t kb2, u32x4 (&w)[WV]) __attribute__((always_inline)) {
+      const uint32_t qo = (uint32_t)n * (uint32_t)ex.rb_i;
+#pragma unroll
+      for (int v = 0; v < WV; ++v)
+        w[v] = ld_region16(rq, qo + (FMT == kFmtInt4 ? kb2 * 64u + (uint32_t)s * 16u
+                                                     : kb2 * 128u + (uint32_t)s * 32u + 16u * v));
+    };
+    auto load = [&](Chunk& ch, int j) __attribute__((always_inline)) {
+      const bool ok = j < nj;
+      const int tk = ok ? wave + kMW * (j / CPT) : 0;
+      const int k0 = ok ? (j % CPT) * CK2 : 0;
+      const int tsk = ok ? wuni(s_task[tk]) : 0;
+      __amdgpu_buffer_rsrc_t rq, rsc;
+      task_rsrc(ok, tsk, rq, rsc);
+      const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
+      if constexpr (SM == 0) {
+        ch.sc[0] = ld_region4(rsc, so);  // the row's one scale
+      } else if constexpr (SM == 1) {
+#pragma unroll
+        for (int kk = 0; kk < CK2; ++kk)
+          ch.sc[kk] = ld_region4(rsc, so + (((uint32_t)(k0 + kk) * 128u + (uint32_t)s * 32u) >> (ex.gshift + 5)) * 4u);
+      } else {  // groups of 64: scale 2 kb2 + s / 2; a 16-byte load from
+                // 2 k0 + 4 v + s / 2 holds those of kb2 = k0 + 2v, k0 + 2v + 1
+                // in its words 0 and 2
+#pragma unroll
+        for (int v = 0; v < CK2 / 2; ++v) ch.sc4[v] = ld_region16(rsc, so + (uint32_t)(2 * k0 + 4 * v + (s >> 1)) * 4u);
+      }
+#pragma unroll
+      for (int kk = 0; kk < CK2; ++kk) wload(rq, (uint32_t)(k0 + kk), ch.w[kk]);
+    };
+
+    auto bconv = [&](const u32x4 (&w)[WV], int hh) __attribute__((always_inline)) {
+      if constexpr (FMT == kFmtInt4) {
+        const uint32_t w0 = w[0][2 * hh], w1 = w[0][2 * hh + 1];
+        return u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+      } else {
+        return w[hh];
+      }
+    };
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    bool xseen = false;  // the round's slots are written (all waves)
+    auto wait_slots = [&]() __attribute__((always_inline)) {
+      if (!xseen) {
+        while (__hip_atomic_load(&s_xready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kMW)
+          __builtin_amdgcn_s_sleep(1);
+        xseen = true;
+      }
+    };
+    // o[n] of a task from the lane's accumulators: its columns combined, then
+    // the four lanes of the row (k-slots) summed
+    auto row_value = [&](const float (&c)[4]) __attribute__((always_inline)) {
+      float v = __builtin_fmaf(c[1], 256.f, c[0]) + __builtin_fmaf(c[3], 256.f, c[2]) * (1.f / 32768.f);
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      return v;
+    };
+    uint64_t tmore = 0;  // this wave's tasks (by index) with groups of more than two planes
+
+    auto compute = [&](Chunk& ch, int j) __attribute__((always_inline)) {
+      const int ti = j / CPT, tk = wave + kMW * ti;
+      const int part_i = j % CPT, k0 = part_i * CK2;
+      const int tsk = wuni(s_task[tk]);
+      const int pi = tsk >> 12, tile = tsk & 0xFFF;
+      const int pr = slot_of(pi);
+      const uint8_t* rp = rec + (size_t)pr * NGL * kRecBytes;
+      if (part_i == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = 0.f;
+        // steps of this task with further planes: bit 2 kb2 + hh for a
+        // group G = 8 kb2 + 2 s + hh with P > 2
+        xm0 = xm1 = 0;
+        for (int g0 = 0; g0 < NG; g0 += 64) {
+          const int g = g0 + lane;
+          const bool f = g < NG && (*reinterpret_cast<const int*>(rp + (size_t)g * kRecBytes + 84) & 0xFF) > 2;
+          const uint64_t m = __ballot(f);
+          if (m != 0) {
+#pragma unroll
+            for (int bk = 0; bk < 8; ++bk) {  // lanes 8 bk .. 8 bk + 7: groups of k block g0 / 8 + bk
+              const uint32_t mb = (uint32_t)(m >> (8 * bk)) & 0xFFu;
+              const int step = 2 * (g0 / 8 + bk);
+              const uint32_t bits = ((mb & 0x55u) ? 1u : 0u) | ((mb & 0xAAu) ? 2u : 0u);
+              if (step < 32) xm0 |= bits << step;
+              else xm1 |= bits << (step - 32);
+            }
+          }
+        }
+        if ((xm0 | xm1) != 0) tmore |= 1ull << ti;
+      }
+      const uint32_t xm = (uint32_t)((((uint64_t)xm1 << 32) | xm0) >> (2 * k0)) & ((1u << (2 * CK2)) - 1u);
+      if (xm != 0) wait_slots();
+      // scales of the chunk taken here (all words of their loads in use)
+      if constexpr (SM == 2)
+#pragma unroll
+        for (int v = 0; v < CK2 / 2; ++v) asm volatile("" : "+v"(ch.sc4[v]));
+      auto scale_of = [&](int kk) __attribute__((always_inline)) {
+        return SM == 2 ? __uint_as_float(ch.sc4[kk / 2][2 * (kk & 1)]) : (SM == 0 ? 1.f : ch.sc[kk]);
+      };
+      const bool diag = (n >> 2) == s;
+      // software pipeline over the 2 CK2 steps: the LDS reads of step st + 1
+      // are issued before the matrix instruction of step st, whose result is
+      // taken after that of step st + 1 is issued (same summation order)
+      struct StepIn {
+        u32x4 av, cin;
+        float hf;
+        int pinfo;
+      };
+      auto rd = [&](int st_) __attribute__((always_inline)) {
+        const int G = 8 * (k0 + (st_ >> 1)) + 2 * s + (st_ & 1);
+        const uint8_t* rg = rp + (size_t)G * kRecBytes;
+        StepIn r;
+        r.av = *reinterpret_cast<const u32x4*>(diag ? rg + 16 * (n & 3) : zrec);
+        r.cin = *reinterpret_cast<const u32x4*>(rg + 64);
+        const uint2 hp = *reinterpret_cast<const uint2*>(rg + 80);
+        r.hf = __uint_as_float(hp.x);
+        r.pinfo = (int)hp.y;
+        return r;
+      };
+      StepIn cur = rd(0);
+      v4i cp = {0, 0, 0, 0};
+      float fp = 0.f;
+#pragma unroll
+      for (int st_ = 0; st_ < 2 * CK2; ++st_) {
+        StepIn nx = cur;
+        if (st_ + 1 < 2 * CK2) nx = rd(st_ + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4 bw = bconv(ch.w[st_ >> 1], st_ & 1);
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, cur.av), __builtin_bit_cast(v4i, bw),
+                                                            __builtin_bit_cast(v4i, cur.cin), 0, 0, 0);
+        const float f = scale_of(st_ >> 1) * cur.hf;
+        if (st_ > 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)cp[i], fp, acc[i]);
+        if ((xm >> st_) & 1) {
+          // plane pair 1 of the step's groups that have a slot (zero record
+          // for the others: they are added after the chunks)
+          const int slot = (cur.pinfo >> 8) - 1;
+          const bool has = (cur.pinfo & 0xFF) > 2 && slot >= 0;
+          const uint8_t* xg = has ? xrec + (size_t)slot * kRecBytes : zrec;
+          const u32x4 xa = *reinterpret_cast<const u32x4*>(diag ? xg + 16 * (n & 3) : zrec);
+          const u32x4 xc = *reinterpret_cast<const u32x4*>(xg + 64);
+          const float xh = *reinterpret_cast<const float*>(xg + 80);
+          const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa), __builtin_bit_cast(v4i, bw),
+                                                               __builtin_bit_cast(v4i, xc), 0, 0, 0);
+          const float f2 = scale_of(st_ >> 1) * xh;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)c2[i], f2, acc[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        cp = c;
+        fp = f;
+        cur = nx;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)cp[i], fp, acc[i]);
+      if (part_i == CPT - 1) {
+        const float v = row_value(acc);
+        const int row = 16 * tile + n;
+        const int pair = wuni(R.upair[pi]);
+        if (s == 0 && row < nr) part[(size_t)row * np + pair] = SM == 0 ? v * ch.sc[0] : v;
+      }
+    };
+
+    load(A, 0);
+    load(B, 1);
+    // the thread's plane pair 1 records into their slots, then this wave is
+    // counted as done (its weights were requested first)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (xslot[j] >= 0) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) reinterpret_cast<u32x4*>(xrec + (size_t)xslot[j] * kRecBytes)[k] = xr[j][k];
+      }
+    if (lane == 0) __hip_atomic_fetch_add(&s_xready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int j = 0; j < nj; j += 2) {
+      compute(A, j);
+      load(A, j + 2);
+      if (j + 1 >= nj) break;
+      compute(B, j + 1);
+      load(B, j + 3);
+    }
+
+    // planes past the slots: plane pairs 2 and up, and plane pair 1 of groups
+    // without a slot, added to the task's rows (rare)
+    if (tmore != 0) {
+      wait_slots();
+      for (int ti = 0; ti < myt; ++ti) {
+        if (((tmore >> ti) & 1) == 0) continue;
+        const int tsk = wuni(s_task[wave + kMW * ti]);
+        const int pi = tsk >> 12, tile = tsk & 0xFFF;
+        const int pair = wuni(R.upair[pi]);
+        const uint8_t* rp = rec + (size_t)slot_of(pi) * NGL * kRecBytes;
+        uint32_t tm0 = 0, tm1 = 0;
+        for (int g0 = 0; g0 < NG; g0 += 64) {
+          const int g = g0 + lane;
+          const int pinfo = g < NG ? *reinterpret_cast<const int*>(rp + (size_t)g * kRecBytes + 84) : 0;
+          const int pc = pinfo & 0xFF;
+          const uint64_t m = __ballot(pc > 4 || (pc > 2 && (pinfo >> 8) == 0));
+          for (int bk = 0; bk < 8; ++bk) {
+            const uint32_t mb = (uint32_t)(m >> (8 * bk)) & 0xFFu;
+            const int step = 2 * (g0 / 8 + bk);
+            const uint32_t bits = ((mb & 0x55u) ? 1u : 0u) | ((mb & 0xAAu) ? 2u : 0u);
+            if (step < 32) tm0 |= bits << step;
+            else tm1 |= bits << (step - 32);
+          }
+        }
+        uint64_t tm = ((uint64_t)tm1 << 32) | tm0;
+        if (tm == 0) continue;
+        __amdgpu_buffer_rsrc_t rq, rsc;
+        task_rsrc(true, tsk, rq, rsc);
+        const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
+        float tacc[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool diag = (n >> 2) == s;
+        while (tm != 0) {
+          const int b = __builtin_ctzll(tm);
+          tm &= tm - 1;
+          const uint32_t kb2 = (uint32_t)(b >> 1);
+          const int hh = b & 1;
+          u32x4 w[WV];
+          wload(rq, kb2, w);
+          float sc = 1.f;
+          if constexpr (SM == 1) sc = ld_region4(rsc, so + ((kb2 * 128u + (uint32_t)s * 32u) >> (ex.gshift + 5)) * 4u);
+          if constexpr (SM == 2) sc = ld_region4(rsc, so + (2u * kb2 + (uint32_t)(s >> 1)) * 4u);
+          const u32x4 bw = bconv(w, hh);
+          const int G = 8 * (int)kb2 + 2 * s + hh;
+          const int pinfo = *reinterpret_cast<const int*>(rp + (size_t)G * kRecBytes + 84);
+          const int pc = pinfo & 0xFF;
+          const int qlo = (pinfo >> 8) != 0 ? 2 : 1;
+          int nq = (pc + 1) / 2;
+          nq = max(nq, __shfl_xor(nq, 16, 64));
+          nq = wuni(max(nq, __shfl_xor(nq, 32, 64)));
+          for (int q = 1; q < nq; ++q) {
+            const bool act = q >= qlo && 2 * q < pc;
+            const uint32_t ro = act ? (uint32_t)(((int64_t)pair * kRecPairs + q) * NGP + G) * kRecBytes : kOutside;
+            const u32x4 xa = __builtin_amdgcn_raw_buffer_load_b128(rall, diag ? ro + 16u * (uint32_t)(n & 3) : kOutside, 0, 0);
+            const u32x4 xc = __builtin_amdgcn_raw_buffer_load_b128(rall, ro + 64u, 0, 0);
+            const float xh = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rall, ro + 80u, 0, 0));
+            const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa), __builtin_bit_cast(v4i, bw),
+                                                                 __builtin_bit_cast(v4i, xc), 0, 0, 0);
+            const float f2 = sc * xh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tacc[i] = __builtin_fmaf((float)c2[i], f2, tacc[i]);
+          }
+        }
+        float v = row_value(tacc);
+        if constexpr (SM == 0) v *= ld_region4(rsc, so);
+        const int row = 16 * tile + n;
+        if (s == 0 && row < nr) part[(size_t)row * np + pair] += v;
+      }
+    }
+    pb = pe;
+    ub = ue;
+    if (pb < nvalid && ub < nu && R.ustart[ub] > pb) --ub;  // an expert split over rounds continues
   }
   __syncthreads();
   // y_t[r] = sum over valid slots j, in order, of w_tj * part[r][t k + j]
@@ -557,95 +1010,114 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a) {
   }
 }
 
-// caller-supplied fp32 h [T*k][I] -> digit planes, one wave per (pair, group)
+// caller-supplied fp32 h [T*k][I] -> records, one wave per (pair, group)
 template <int FMT>
-__global__ __launch_bounds__(256) void h_planes_kernel(MoeDecArgs a, int ngroups_total) {
+__global__ __launch_bounds__(256) void h_records_kernel(MoeDecArgs a, int ngroups_total) {
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= ngroups_total) return;
-  const int NG = (a.ex.I + 15) / 16;
+  const int NG = (a.ex.I + 15) / 16, NGP = dn_ngp(a.ex.I);
   const int pair = g / NG, gi = g - pair * NG;
   const int lane = threadIdx.x & 63;
   const int r = gi * 16 + lane;
   const float v = (lane < 16 && r < a.ex.I) ? a.h[(int64_t)pair * a.ex.I + r] : 0.f;
-  wave_h_planes<FMT>(v, a.hq + (int64_t)g * (kPlaneMax * 8), a.hf + g, a.hp + g);
+  wave_h_records<FMT>(v, a.hrec + (((int64_t)pair * kRecPairs) * NGP + gi) * kRecBytes, (size_t)NGP * kRecBytes);
 }
 
 // ---- launchers ------------------------------------------------------------------------
 
+// chunk positions per lane of the gate+up kernel instantiated for rows of
+// kch chunks (0: none)
+int gu_cpl(int kch) {
+  const int c = (kch + 63) / 64;
+  if (c <= 4) return c;
+  if (c <= 6) return 6;
+  if (c <= 8) return 8;
+  return 0;
+}
+
+// LDS bytes of the gate+up kernel: two planes of digit words and a factor per
+// chunk position, for T tokens
+size_t gu_lds(int fmt, int T, int H) {
+  const int per = fmt == kFmtInt4 ? 32 : 16;
+  const size_t kchp = (size_t)64 * gu_cpl(H / per);
+  return (size_t)2 * T * kchp * (fmt == kFmtInt4 ? 16 : 8) * 4 + (size_t)T * kchp * 4;
+}
+
 template <int FMT, int XT, bool GROUPED>
 hipError_t launch_gu(const MoeDecArgs& a, int cus, hipStream_t st) {
   constexpr int PER = per_chunk<FMT>();
-  const int KCH = a.ex.H / PER;
-  const size_t lds = (size_t)2 * a.T * KCH * x_words<FMT>() * 4 + (size_t)a.T * KCH * 4;
-  if (lds > kDecLdsMax) return hipErrorNotSupported;
+  const int cpl = gu_cpl(a.ex.H / PER);
+  const size_t lds = gu_lds(FMT, a.T, a.ex.H);
+  if (cpl == 0 || lds > kDecLdsMax || a.T * 64 * cpl > 2 * kGT) return hipErrorNotSupported;
   const int nunits_max = a.T * a.topk * ((a.ex.I + kHT - 1) / kHT);
   const int blocks = max(1, min(cus, nunits_max));
-  const int cpl = (KCH + 63) / 64;
-#define QM_GU(C)                                                                                         \
-  hipLaunchKernelGGL((moe_gu_kernel<FMT, XT, GROUPED, C>), dim3(blocks), dim3(kGT), lds, st, a); \
+  // two register buffers of weights (the next unit loading while one is
+  // computed) where they fit the 256 registers of each of the 8 waves
+#define QM_GU(C, NBUF)                                                                                         \
+  hipLaunchKernelGGL((moe_gu_kernel<FMT, XT, GROUPED, C, NBUF>), dim3(blocks), dim3(kGT), lds, st, a); \
   return hipGetLastError();
   switch (cpl) {
-    case 1: { QM_GU(1) }
-    case 2: { QM_GU(2) }
-    case 3: { QM_GU(3) }
-    case 4: { QM_GU(4) }
+    case 1: { QM_GU(1, 2) }
+    case 2: { QM_GU(2, 2) }
+    case 3: { QM_GU(3, 2) }
+    case 4: { QM_GU(4, 1) }
+    case 6: { QM_GU(6, 1) }
+    case 8: { QM_GU(8, 1) }
     default: break;
   }
-  if (cpl <= 6) { QM_GU(6) }
-  if (cpl <= 8) { QM_GU(8) }
 #undef QM_GU
   return hipErrorNotSupported;
 }
 
-template <int FMT, bool GROUPED>
-hipError_t launch_down(const MoeDecArgs& a, int cus, hipStream_t st) {
-  const int KCH = a.ex.I / per_chunk<FMT>();
-  const int Rb = (a.ex.H + cus - 1) / cus;      // rows per workgroup
-  const int blocks = (a.ex.H + Rb - 1) / Rb;    // every workgroup has rows
-  const size_t lds = (size_t)Rb * a.T * a.topk * 4;
-  if (lds > kDecLdsMax) return hipErrorNotSupported;
-#define QM_DN(L_, C, NB_)                                                                                    \
-  hipLaunchKernelGGL((moe_down_kernel<FMT, GROUPED, L_, C, NB_>), dim3(blocks), dim3(kMT), lds, st, a); \
+// Down launch plan: rows per workgroup, pairs per round, slots for plane
+// pair 1 records and the dynamic LDS bytes; false when the shape does not fit.
+struct DnPlan {
+  int Rb, blocks, PR, xcap;
+  size_t lds;
+};
+bool dn_plan(int fmt, int T, int topk, int H, int I, int cus, DnPlan& p) {
+  if (cus < 1 || H < 1 || I < 1) return false;
+  p.Rb = (H + cus - 1) / cus;
+  p.blocks = (H + p.Rb - 1) / p.Rb;  // every workgroup has rows
+  const int np = T * topk;
+  if ((p.Rb + 15) / 16 > 4096 || (I + 127) / 128 > 32) return false;  // task and step bit fields
+  const size_t fixed = ((size_t)p.Rb * np * 4 + 15) / 16 * 16 + kRecBytes;  // part, zero record
+  const size_t per_pair = (size_t)dn_ngl(fmt, I) * kRecBytes;
+  if (fixed + per_pair > kDnLdsMax) return false;
+  p.PR = (int)std::min<size_t>((size_t)np, (kDnLdsMax - fixed) / per_pair);  // pairs per round
+  const size_t used = fixed + (size_t)p.PR * per_pair;
+  p.xcap = (int)std::min<size_t>(2 * kMT, (kDnLdsMax - used) / kRecBytes);
+  p.lds = used + (size_t)p.xcap * kRecBytes;
+  return true;
+}
+
+template <int FMT>
+hipError_t launch_down(const MoeDecArgs& a, int gs, int cus, hipStream_t st) {
+  DnPlan p;
+  if (!dn_plan(FMT, a.T, a.topk, a.ex.H, a.ex.I, cus, p)) return hipErrorNotSupported;
+#define QM_DN(SM_)                                                                                         \
+  hipLaunchKernelGGL((moe_down_kernel<FMT, SM_>), dim3(p.blocks), dim3(kMT), p.lds, st, a, p.PR, p.xcap); \
   return hipGetLastError();
-  // NB row passes in flight per wave: the whole row block when it fits
-  const int npass16 = (Rb + 3) / 4, npass32 = (Rb + 1) / 2;
-  if (KCH <= 16) {
-    if (npass16 <= 8) { QM_DN(16, 1, 8) }
-    QM_DN(16, 1, 16)
-  }
-  if (KCH <= 32) {
-    if (npass32 <= 12) { QM_DN(32, 1, 12) }
-    QM_DN(32, 1, 16)
-  }
-  if (KCH <= 64) {
-    if (Rb <= 12) { QM_DN(64, 1, 12) }
-    QM_DN(64, 1, 24)
-  }
-  if (KCH <= 128) { QM_DN(64, 2, 8) }
+  if (gs == 0) { QM_DN(0) }
+  if (gs == 64) { QM_DN(2) }
+  QM_DN(1)
 #undef QM_DN
-  return hipErrorNotSupported;
 }
 
 }  // namespace
 
 size_t moe_decode_ws_bytes(int T, int topk, int H, int I) {
   const size_t P = (size_t)T * topk;
-  const size_t NG = (size_t)(I + 15) / 16;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  return al(P * NG * kPlaneMax * 32) + al(P * NG * 4) + al(P * NG * 4) + al(P * (size_t)I * 8);
+  return al(P * kRecPairs * dn_ngp(I) * kRecBytes) + al(P * (size_t)I * 8);
 }
 
 void moe_decode_ws_split(MoeDecArgs& a, void* ws) {
   const size_t P = (size_t)a.T * a.topk;
-  const size_t NG = (size_t)(a.ex.I + 15) / 16;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   char* p = static_cast<char*>(ws);
-  a.hq = reinterpret_cast<uint32_t*>(p);
-  p += al(P * NG * kPlaneMax * 32);
-  a.hf = reinterpret_cast<float*>(p);
-  p += al(P * NG * 4);
-  a.hp = reinterpret_cast<int*>(p);
-  p += al(P * NG * 4);
+  a.hrec = reinterpret_cast<uint8_t*>(p);
+  p += al(P * kRecPairs * dn_ngp(a.ex.I) * kRecBytes);
   a.ab = reinterpret_cast<float*>(p);
 }
 
@@ -653,17 +1125,20 @@ bool moe_decode_supported(int fmt, int T, int topk, const ExpertArgs& e) {
   if (T < 1 || T * topk > kMaxPairs) return false;
   const int per = fmt == kFmtInt4 ? 32 : 16;
   const int kh = e.H / per, ki = e.I / per;
-  if ((kh + 63) / 64 > 8 || ki > 128) return false;
-  if ((size_t)2 * T * kh * (fmt == kFmtInt4 ? 16 : 8) * 4 + (size_t)T * kh * 4 > (size_t)kDecLdsMax) return false;
-  return true;
+  (void)ki;
+  if (gu_cpl(kh) == 0) return false;
+  int cus = 0;
+  DnPlan p;
+  if (device_cus(&cus) != hipSuccess || !dn_plan(fmt, T, topk, e.H, e.I, cus, p)) return false;
+  return gu_lds(fmt, T, e.H) <= kDecLdsMax && T * 64 * gu_cpl(kh) <= 2 * kGT;
 }
 
 // largest token count per pass whose x digit planes fit the LDS budget
 int moe_decode_tokens_per_pass(int fmt, int topk, const ExpertArgs& e) {
   const int per = fmt == kFmtInt4 ? 32 : 16;
-  const int kh = e.H / per;
-  const size_t per_tok = (size_t)2 * kh * (fmt == kFmtInt4 ? 16 : 8) * 4 + (size_t)kh * 4;
-  int t = (int)(kDecLdsMax / per_tok);
+  if (gu_cpl(e.H / per) == 0) return 0;
+  int t = (int)(kDecLdsMax / gu_lds(fmt, 1, e.H));
+  t = min(t, 2 * kGT / (64 * gu_cpl(e.H / per)));  // two x groups per thread when staging
   t = min(t, kDecMaxTokens);
   t = min(t, kMaxPairs / topk);
   return max(t, 0);
@@ -688,15 +1163,17 @@ hipError_t launch_moe_down2(int fmt, bool grouped, const MoeDecArgs& a, bool h_f
   if (h_from_caller) {
     const int ng = a.T * a.topk * ((a.ex.I + 15) / 16);
     if (fmt == kFmtInt4)
-      hipLaunchKernelGGL(h_planes_kernel<kFmtInt4>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
+      hipLaunchKernelGGL(h_records_kernel<kFmtInt4>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
     else
-      hipLaunchKernelGGL(h_planes_kernel<kFmtInt8>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
+      hipLaunchKernelGGL(h_records_kernel<kFmtInt8>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (fmt == kFmtInt4) return grouped ? launch_down<kFmtInt4, true>(a, cus, st) : launch_down<kFmtInt4, false>(a, cus, st);
+  // the down matrices' scale group size (0: one scale per row)
+  const int gs = (grouped && a.ex.G_i > 1) ? (32 << a.ex.gshift) : 0;
+  if (fmt == kFmtInt4) return launch_down<kFmtInt4>(a, gs, cus, st);
   if (grouped) return hipErrorNotSupported;
-  return launch_down<kFmtInt8, false>(a, cus, st);
+  return launch_down<kFmtInt8>(a, 0, cus, st);
 }
 
 }  // namespace qm

@@ -130,24 +130,26 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 }
 
 // Exact integer sum over one 16-byte chunk of int4 weights (w, each word
-// already XOR 0x88888888) against one plane of its 32-group (x[0..15]).
-// One independent chain per digit, combined at the end (the chains overlap
-// in the pipeline instead of each product waiting for the previous one).
+// already XOR 0x88888888) against one plane of its 32-group (x[0..15]):
+// sum_d 16^d T_d with T_d the digit-d products, accumulated from the top
+// digit down (t <- 16 t + T_d), so that the accumulator of each dot
+// instruction carries the running sum (|partial sums| stay below 2^22).
+__device__ __forceinline__ int shl4(int t) { return (int)((uint32_t)t << 4); }
 __device__ __forceinline__ int gdot_i4(const u32x4& w, const uint32_t* x) {
-  int t[4];
+  int t = sdot8(w[3], x[12 + 3], sdot8(w[2], x[8 + 3], sdot8(w[1], x[4 + 3], sdot8(w[0], x[3], 0))));
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-    t[d] = sdot8(w[0], x[d], sdot8(w[1], x[4 + d], sdot8(w[2], x[8 + d], sdot8(w[3], x[12 + d], 0))));
-  return (int)((uint32_t)t[0] + ((uint32_t)t[1] << 4) + ((uint32_t)t[2] << 8) + ((uint32_t)t[3] << 12));
+  for (int d = 2; d >= 0; --d)
+    t = sdot8(w[3], x[12 + d], sdot8(w[2], x[8 + d], sdot8(w[1], x[4 + d], sdot8(w[0], x[d], shl4(t)))));
+  return t;
 }
 
 // Exact integer sum over 16 int4 weights (words w0, w1, each XOR
 // 0x88888888) against one plane of their 16-group (x[0..7]: words 4j + d).
 __device__ __forceinline__ int gdot16_i4(uint32_t w0, uint32_t w1, const uint32_t* x) {
-  int t[4];
+  int t = sdot8(w1, x[4 + 3], sdot8(w0, x[3], 0));
 #pragma unroll
-  for (int d = 0; d < 4; ++d) t[d] = sdot8(w0, x[d], sdot8(w1, x[4 + d], 0));
-  return (int)((uint32_t)t[0] + ((uint32_t)t[1] << 4) + ((uint32_t)t[2] << 8) + ((uint32_t)t[3] << 12));
+  for (int d = 2; d >= 0; --d) t = sdot8(w1, x[4 + d], sdot8(w0, x[d], shl4(t)));
+  return t;
 }
 
 // The same for 16 int8 weights (words w[0..3]) against a 16-group's plane.
@@ -221,6 +223,32 @@ __device__ __forceinline__ void stage_group(const void* __restrict__ x, int64_t 
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       if (pp >= np) break;
+      uint32_t wd[WPS];
+      if constexpr (FMT == kFmtInt4)
+        plane_words8_i4(r, wd);
+      else
+        plane_words4_i8(r, wd);
+#pragma unroll
+      for (int k = 0; k < WPS; ++k) dst[pp * pstride + j * WPS + k] = wd[k];
+    }
+  }
+}
+
+// The same from the group's N values already in registers (planes p0 and
+// p0 + 1); v is consumed.
+template <int FMT, int N>
+__device__ __forceinline__ void stage_group_vals(float (&v)[N], int E, int p0, uint32_t* __restrict__ dst,
+                                                 size_t pstride) {
+  constexpr int SB = FMT == kFmtInt4 ? 8 : 4;
+  constexpr int WPS = FMT == kFmtInt4 ? 4 : 2;
+#pragma unroll
+  for (int j = 0; j < N / SB; ++j) {
+    float r[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) r[i] = ldexpf(v[j * SB + i], 14 - E);
+    skip_planes(r, p0);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
       uint32_t wd[WPS];
       if constexpr (FMT == kFmtInt4)
         plane_words8_i4(r, wd);

@@ -377,7 +377,7 @@ int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
   MoeDecArgs a = dec_args(expert_args(ex), x, x_dtype, 0, n_tokens, topk_ids, nullptr, top_k, h, nullptr, workspace);
-  a.hq = nullptr;  // h only: no digit planes for a down pass
+  a.hrec = nullptr;  // h only: no records for a down pass
   const hipError_t err = launch_moe_gate_up2(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
