@@ -1127,9 +1127,12 @@ bool moe_decode_supported(int fmt, int T, int topk, const ExpertArgs& e) {
   const int kh = e.H / per, ki = e.I / per;
   (void)ki;
   if (gu_cpl(kh) == 0) return false;
+  // the down plan on this device's compute units (without a device: checked
+  // for 256, so that argument checks do not depend on one being present)
   int cus = 0;
+  if (device_cus(&cus) != hipSuccess) cus = 256;
   DnPlan p;
-  if (device_cus(&cus) != hipSuccess || !dn_plan(fmt, T, topk, e.H, e.I, cus, p)) return false;
+  if (!dn_plan(fmt, T, topk, e.H, e.I, cus, p)) return false;
   return gu_lds(fmt, T, e.H) <= kDecLdsMax && T * 64 * gu_cpl(kh) <= 2 * kGT;
 }
 
