@@ -573,39 +573,62 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
 //
 // A workgroup owns output rows [r0, r0 + nr) (tiles of 16).  A task is (a
 // routed pair, a tile); waves take the tasks in turn, their k blocks in
-// chunks of CK2, two chunks in flight per wave (registers A and B).  The
-// records (plane pair 0) of the pairs are staged in LDS, zero past the
-// pair's groups up to whole chunks; with one round for all pairs (the
-// usual case) a pair's LDS slot is its index and its records are requested
-// at the start with the routing ids, ahead of any weights.
+// chunks of CK2, kNB chunks in flight per wave (a ring of register
+// buffers).  The records (plane pair 0) of the pairs are staged in LDS, zero
+// past the pair's groups up to whole chunks; with one round for all pairs
+// (the usual case) a pair's LDS slot is its index and its records are
+// requested at the start with the routing ids.  Each step's LDS reads sit at
+// fixed offsets from a per-lane base (lanes off the diagonal read a zero
+// block), issued one step ahead of the matrix instruction.
 //
 // Groups with more than two planes: the thread that stages such a group's
-// record also requests its plane pair 1 record, gets a slot in item order
-// (a prefix count over the waves) and writes it there once its own weights
-// are requested; a step with such groups then adds that plane pair inside
-// its chunk.  Planes beyond those (and groups past the slots) are added
-// after the wave's chunks, reloading the few weights they need.
-// Per-(row, pair) results meet in LDS and every output is y_t = sum_j w_tj
-// o_tj in slot order, so y does not depend on timing.
-constexpr int kMaxTasks = 512;                  // tasks per round
+// record also requests its plane pair 1 record (before any weights), gets a
+// slot in item order (a prefix count over the waves), writes it there and
+// enters the slot in a per-(pair, chunk, k-slot) table of the chunk's eight
+// steps (others point at a zero record).  A chunk with such groups runs
+// every step with a second instruction on its plane pair 1 records, their
+// addresses read from that table at the chunk's start.  Planes beyond those
+// (and groups past the slots) are added after the wave's chunks, reloading
+// the few weights they need.  Per-(row, pair) results meet in LDS and every
+// output is y_t = sum_j w_tj o_tj in slot order, so y does not depend on
+// timing.
+constexpr int kMaxTasksPerWave = 64;            // tasks of a wave in one round (one per lane)
+constexpr int kNB = 4;                          // chunks in flight per wave
 constexpr uint32_t kOutside = 0x80000000u;      // a buffer offset past every record: loads zeros
 constexpr size_t kDnLdsMax = 144 * 1024;        // dynamic LDS of the down kernel
 
-__host__ __device__ constexpr int dn_ck2(int fmt) { return fmt == kFmtInt4 ? 8 : 4; }
+__host__ __device__ constexpr int dn_ck2(int fmt) { return fmt == kFmtInt4 ? 4 : 2; }
 // record slots per pair in LDS: whole chunks of k blocks
 __host__ __device__ constexpr int dn_ngl(int fmt, int I) {
   return 8 * dn_ck2(fmt) * (((I + 127) / 128 + dn_ck2(fmt) - 1) / dn_ck2(fmt));
+}
+// zero block read by the lanes off the diagonal: the largest step offset + 16
+__host__ __device__ constexpr int dn_zblock(int fmt) { return ((8 * (dn_ck2(fmt) - 1) + 1) * kRecBytes + 16 + 15) / 16 * 16; }
+
+// Flags of 64 consecutive groups (bit i: group g0 + i, g0 a multiple of 64)
+// to flags of their 16 steps: bit 2 b + h is set when a group 8 b + 2 s + h
+// (s < 4) of k block g0 / 8 + b is flagged.
+__device__ __forceinline__ uint32_t step_bits(uint64_t m) {
+  uint64_t e = m & 0x5555555555555555ull, o = (m >> 1) & 0x5555555555555555ull;
+  e |= e >> 2;
+  e |= e >> 4;  // bit 8 b: any even group of byte b
+  o |= o >> 2;
+  o |= o >> 4;
+  uint64_t z = (e & 0x0101010101010101ull) | ((o & 0x0101010101010101ull) << 1);  // 2 bits at 8 b
+  z = (z | (z >> 6)) & 0x000F000F000F000Full;   // 4 bits at 16 c
+  z = (z | (z >> 12)) & 0x000000FF000000FFull;  // 8 bits at 32 d
+  return (uint32_t)(z | (z >> 24)) & 0xFFFFu;
 }
 
 // SM: weight scales.  0: one per row; 1: per group (any size); 2: groups of 64.
 template <int FMT, int SM>
 __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int xcap) {
   constexpr int CK2 = dn_ck2(FMT);
+  constexpr int NS = 2 * CK2;                  // steps per chunk
   constexpr int WV = FMT == kFmtInt4 ? 1 : 2;  // 16-byte weight loads per lane and k block
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ Route R;
-  __shared__ int s_task[kMaxTasks];
-  __shared__ int s_ntasks, s_xready, s_cnt[2][kMW];
+  __shared__ int s_xready, s_cnt[2][kMW];
   const ExpertArgs& ex = a.ex;
   const int H = ex.H, I = ex.I;
   const int np = a.T * a.topk;
@@ -613,13 +636,17 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
   const int CPT = (NK2 + CK2 - 1) / CK2;  // chunks per task
   const int wave = wuni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, s = lane >> 4;
+  const bool diag = (n >> 2) == s;
   const int Rb = (H + gridDim.x - 1) / gridDim.x;
   const int r0 = blockIdx.x * Rb, nr = min(Rb, H - r0);
   const int ntile = (nr + 15) / 16;
-  float* part = reinterpret_cast<float*>(lds);                                             // [Rb][np]
-  uint8_t* rec = reinterpret_cast<uint8_t*>(lds + ((size_t)Rb * np * 4 + 15) / 16 * 16);  // [PR][NGL][96]
-  const uint8_t* zrec = rec + (size_t)PR * NGL * kRecBytes;                                // a zero record
-  uint8_t* xrec = const_cast<uint8_t*>(zrec) + kRecBytes;                                  // [xcap][96]
+  // LDS: part [Rb][np] | records [PR][NGL] | zero block | step table
+  // [PR][CPT][4] of 8 slot numbers | slots [xcap + 1] (the last: zeros)
+  float* part = reinterpret_cast<float*>(lds);
+  uint8_t* rec = reinterpret_cast<uint8_t*>(lds + ((size_t)Rb * np * 4 + 15) / 16 * 16);
+  uint8_t* zblk = rec + (size_t)PR * NGL * kRecBytes;
+  uint16_t* xtab = reinterpret_cast<uint16_t*>(zblk + dn_zblock(FMT));
+  uint8_t* xrec = reinterpret_cast<uint8_t*>(xtab + (size_t)PR * CPT * 4 * 8);
   // the records of every pair: plane pairs q of pair p at (p kRecPairs + q) NGP
   const uint32_t rec_bytes = (uint32_t)((size_t)np * kRecPairs * NGP * kRecBytes);
   const __amdgpu_buffer_rsrc_t rall = region_rsrc(a.hrec, rec_bytes);
@@ -652,18 +679,48 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
     build_route(id_t, w_t, np, ex.E, R);
   }
   const int nu = R.nu, nvalid = R.ustart[nu];
-  if (threadIdx.x < kRecBytes / 4) reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(zrec))[threadIdx.x] = 0u;
+  // the zero block and the zero slot record
+  for (int i = threadIdx.x; i < dn_zblock(FMT) / 4; i += kMT) reinterpret_cast<uint32_t*>(zblk)[i] = 0u;
+  if (threadIdx.x < kRecBytes / 4) reinterpret_cast<uint32_t*>(xrec + (size_t)xcap * kRecBytes)[threadIdx.x] = 0u;
 
   struct Chunk {
-    u32x4 sc4[SM == 2 ? CK2 / 2 : 1];  // groups of 64: whole 16-byte loads
+    u32x4 sc4[SM == 2 ? (CK2 + 1) / 2 : 1];  // groups of 64: whole 16-byte loads
     float sc[SM == 2 ? 1 : CK2];
     u32x4 w[CK2][WV];
   };
-  Chunk A, B;
-  float acc[4];
-  uint32_t xm0 = 0, xm1 = 0;  // the task's steps with further planes (bit 2 kb2 + hh)
+  Chunk ring[kNB];
+  typedef int v4i __attribute__((ext_vector_type(4)));
+
+  auto bconv = [&](const u32x4 (&w)[WV], int hh) __attribute__((always_inline)) {
+    if constexpr (FMT == kFmtInt4) {
+      const uint32_t w0 = w[0][2 * hh], w1 = w[0][2 * hh + 1];
+      return u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+    } else {
+      return w[hh];
+    }
+  };
+  auto mfma = [&](const u32x4& av, const u32x4& bw, const u32x4& cin) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, av), __builtin_bit_cast(v4i, bw),
+                                                 __builtin_bit_cast(v4i, cin), 0, 0, 0);
+  };
+  // a step's four integer columns into the lane's two accumulators: plane
+  // 2q (C0 + 256 C1, exact: below 2^23) and plane 2q + 1 (C2 + 256 C3)
+  float a01 = 0.f, a23 = 0.f;
+  auto accum = [&](const v4i& c, float f) __attribute__((always_inline)) {
+    a01 = __builtin_fmaf((float)(c[0] + (c[1] << 8)), f, a01);
+    a23 = __builtin_fmaf((float)(c[2] + (c[3] << 8)), f, a23);
+  };
+  // o[n] of a task from the lane's accumulators, the four lanes of the row
+  // (k-slots) summed
+  auto row_value = [&](float p01, float p23) __attribute__((always_inline)) {
+    float v = __builtin_fmaf(p23, 1.f / 32768.f, p01);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+  };
 
   int pb = 0, ub = 0;  // first pair and its unique expert of the round
+  bool first = true;
   while (pb < nvalid) {
     // the round: pairs [pb, pe), ending at an expert boundary when one fits
     int pe = min(nvalid, pb + PR);
@@ -672,23 +729,27 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
     if (ue > ub) pe = R.ustart[ue];
     else ue = ub + 1;                                // one expert split over rounds
     const int nit = one ? np * NGL : (pe - pb) * NGL;  // items staged for the round
-    auto slot_of = [&](int pi) __attribute__((always_inline)) { return one ? wuni(R.upair[pi]) : pi - pb; };
     auto pair_of_slot = [&](int pr) __attribute__((always_inline)) { return one ? pr : R.upair[pb + pr]; };
+    // tasks: t = (place in the routing table - pb) ntile + tile; wave w takes
+    // t = w, w + kMW, ...: lane i of the wave holds its task i (expert id;
+    // pair, LDS slot and tile packed)
+    const int ntasks = (pe - pb) * ntile;
+    const int myt = wave < ntasks ? (ntasks - 1 - wave) / kMW + 1 : 0;
+    const int nj = myt * CPT;  // this wave's chunks
+    int tk_e = 0, tk_p = 0;
+    if (lane < myt) {
+      const int t = wave + kMW * lane;
+      const int pi = pb + t / ntile, tile = t % ntile;
+      const int pair = R.upair[pi];
+      tk_e = R.tmp_id[pair];
+      tk_p = (pair << 24) | ((one ? pair : pi - pb) << 16) | tile;
+    }
 
-    __syncthreads();  // the previous round's LDS reads are done
+    if (!first) __syncthreads();  // the previous round's LDS reads are done
     if (threadIdx.x == 0) s_xready = 0;
     if (!one) stage_load(nit, pb, true);
-    // the round's tasks: (place in the routing table, tile), packed
-    if (wave == 0) {
-      const int nt = (pe - pb) * ntile;
-      for (int i0 = 0; i0 < nt; i0 += 64) {
-        const int i = i0 + lane;
-        if (i < nt && i < kMaxTasks) s_task[i] = ((pb + i / ntile) << 12) | (i % ntile);
-      }
-      if (lane == 0) s_ntasks = min(nt, kMaxTasks);
-    }
-    // the thread's first two items: staged, and when they have more than two
-    // planes their plane pair 1 records requested (out of range: zeros)
+    // the thread's first two items with more than two planes: their plane
+    // pair 1 records requested (before any weights; others: zeros, no access)
     u32x4 xr[2][6];
     uint64_t xb[2];
 #pragma unroll
@@ -702,6 +763,60 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
 #pragma unroll
       for (int k = 0; k < 6; ++k) xr[j][k] = __builtin_amdgcn_raw_buffer_load_b128(rall, off + 16u * k, 0, 0);
       if (lane == 0) s_cnt[j][wave] = __popcll(xb[j]);
+    }
+    // every step table entry at the zero slot
+    for (int i = threadIdx.x; i < (one ? np : pe - pb) * CPT * 4 * 8 / 2; i += kMT)
+      reinterpret_cast<uint32_t*>(xtab)[i] = (uint32_t)xcap * 0x10001u;
+
+    // weights of the wave's chunk j: task j / CPT, k blocks from CK2 (j %
+    // CPT); the load cursor (lt, lp) walks j; past the end: empty resources
+    // (loads of zeros)
+    int lt = 0, lp = 0;
+    __amdgpu_buffer_rsrc_t rq = region_rsrc(ex.dq, 0u), rsc = region_rsrc(ex.ds, 0u);
+    auto task_rsrc = [&](int ti) __attribute__((always_inline)) {
+      const bool ok = ti < myt;
+      const int e = __builtin_amdgcn_readlane(tk_e, min(ti, 63));
+      const int tile = __builtin_amdgcn_readlane(tk_p, min(ti, 63)) & 0xFFFF;
+      const int rows = min(16, nr - 16 * tile);
+      const int64_t er0 = (int64_t)e * H + r0 + 16 * tile;
+      rq = region_rsrc(ex.dq + er0 * ex.rb_i, ok ? (uint32_t)(rows * ex.rb_i) : 0u);
+      rsc = region_rsrc(ex.ds + er0 * ex.G_i, ok ? (uint32_t)(rows * ex.G_i * 4) : 0u);
+    };
+    const uint32_t qo = (uint32_t)n * (uint32_t)ex.rb_i + (FMT == kFmtInt4 ? (uint32_t)s * 16u : (uint32_t)s * 32u);
+    const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
+    auto wload = [&](uint32_t kb2, u32x4 (&w)[WV]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int v = 0; v < WV; ++v)
+        w[v] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16u * v, (FMT == kFmtInt4 ? 64u : 128u) * kb2, 2);
+    };
+    auto load = [&](Chunk& ch) __attribute__((always_inline)) {
+      if (lp == 0) task_rsrc(lt);
+      const int k0 = lp * CK2;
+      if constexpr (SM == 0) {
+        ch.sc[0] = ld_region4(rsc, so);  // the row's one scale
+      } else if constexpr (SM == 1) {
+#pragma unroll
+        for (int kk = 0; kk < CK2; ++kk)
+          ch.sc[kk] = ld_region4(rsc, so + (((uint32_t)(k0 + kk) * 128u + (uint32_t)s * 32u) >> (ex.gshift + 5)) * 4u);
+      } else {  // groups of 64: scale 2 kb2 + s / 2; a 16-byte load from
+                // 2 k0 + 4 v + s / 2 holds those of kb2 = k0 + 2v, k0 + 2v + 1
+                // in its words 0 and 2
+#pragma unroll
+        for (int v = 0; v < (CK2 + 1) / 2; ++v)
+          ch.sc4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsc, so + (uint32_t)(s >> 1) * 4u, (uint32_t)(2 * k0 + 4 * v) * 4u, 2);
+      }
+#pragma unroll
+      for (int kk = 0; kk < CK2; ++kk) wload((uint32_t)(k0 + kk), ch.w[kk]);
+      if (++lp == CPT) {
+        lp = 0;
+        ++lt;
+      }
+    };
+
+    // the round's records into LDS
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int it = threadIdx.x + kMT * j;
       if (it < nit) put(it, st[j]);
     }
     for (int it = threadIdx.x + 2 * kMT; it < nit; it += kMT) {  // items past two per thread
@@ -713,78 +828,35 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
       for (int k = 0; k < 6; ++k) v6[k] = src[k];
       put(it, v6);
     }
+    // the first kNB chunks of weights requested
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) load(ring[b]);
     __syncthreads();
-    const int ntasks = s_ntasks;
-    const int myt = wave < ntasks ? (ntasks - 1 - wave) / kMW + 1 : 0;  // this wave's tasks
-    const int nj = myt * CPT;                                            // and chunks
-    // slots of the thread's items with more planes: their rank in item order
-    int xslot[2];
+    // slots of the thread's items with more planes: their rank in item order;
+    // the record marked, the step table entry and the slot written
     {
       int base = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         for (int w = 0; w < kMW; ++w) base += (w < wave) ? s_cnt[j][w] : 0;
-        xslot[j] = base + __popcll(xb[j] & ((1ull << lane) - 1));
+        int slot = base + __popcll(xb[j] & ((1ull << lane) - 1));
         for (int w = wave; w < kMW; ++w) base += s_cnt[j][w];
-        if (((xb[j] >> lane) & 1) == 0 || xslot[j] >= xcap) xslot[j] = -1;
-        if (xslot[j] >= 0) {
-          int* pf = reinterpret_cast<int*>(rec + (size_t)(threadIdx.x + kMT * j) * kRecBytes + 84);
-          *pf = (*pf & 0xFF) | ((xslot[j] + 1) << 8);
+        if (((xb[j] >> lane) & 1) != 0 && slot < xcap) {
+          const int it = threadIdx.x + kMT * j;
+          const int pr = it / NGL, g = it - pr * NGL;
+          int* pf = reinterpret_cast<int*>(rec + (size_t)it * kRecBytes + 84);
+          *pf = (*pf & 0xFF) | ((slot + 1) << 8);
+          const int kb2 = g >> 3, gs = (g >> 1) & 3, step = 2 * (kb2 % CK2) + (g & 1);
+          xtab[(((size_t)pr * CPT + kb2 / CK2) * 4 + gs) * 8 + step] = (uint16_t)slot;
+#pragma unroll
+          for (int k = 0; k < 6; ++k) reinterpret_cast<u32x4*>(xrec + (size_t)slot * kRecBytes)[k] = xr[j][k];
         }
       }
     }
+    // this wave's slots are written
+    if (lane == 0) __hip_atomic_fetch_add(&s_xready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
-    // chunk j of this wave: task wave + kMW (j / CPT), k blocks from
-    // CK2 (j % CPT); past the end: empty resources (loads of zeros)
-    auto task_rsrc = [&](bool ok, int tsk, __amdgpu_buffer_rsrc_t& rq, __amdgpu_buffer_rsrc_t& rsc)
-                         __attribute__((always_inline)) {
-      const int pi = tsk >> 12, tile = tsk & 0xFFF;
-      const int rows = min(16, nr - 16 * tile);
-      const int64_t er0 = (int64_t)(ok ? wuni(R.tmp_id[wuni(R.upair[pi])]) : 0) * H + r0 + 16 * tile;
-      rq = region_rsrc(ex.dq + er0 * ex.rb_i, ok ? (uint32_t)(rows * ex.rb_i) : 0u);
-      rsc = region_rsrc(ex.ds + er0 * ex.G_i, ok ? (uint32_t)(rows * ex.G_i * 4) : 0u);
-    };
-    auto wload = [&](__amdgpu_buffer_rsrc_t rq, uint32_t kb2, u32x4 (&w)[WV]) __attribute__((always_inline)) {
-      const uint32_t qo = (uint32_t)n * (uint32_t)ex.rb_i;
-#pragma unroll
-      for (int v = 0; v < WV; ++v)
-        w[v] = ld_region16(rq, qo + (FMT == kFmtInt4 ? kb2 * 64u + (uint32_t)s * 16u
-                                                     : kb2 * 128u + (uint32_t)s * 32u + 16u * v));
-    };
-    auto load = [&](Chunk& ch, int j) __attribute__((always_inline)) {
-      const bool ok = j < nj;
-      const int tk = ok ? wave + kMW * (j / CPT) : 0;
-      const int k0 = ok ? (j % CPT) * CK2 : 0;
-      const int tsk = ok ? wuni(s_task[tk]) : 0;
-      __amdgpu_buffer_rsrc_t rq, rsc;
-      task_rsrc(ok, tsk, rq, rsc);
-      const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
-      if constexpr (SM == 0) {
-        ch.sc[0] = ld_region4(rsc, so);  // the row's one scale
-      } else if constexpr (SM == 1) {
-#pragma unroll
-        for (int kk = 0; kk < CK2; ++kk)
-          ch.sc[kk] = ld_region4(rsc, so + (((uint32_t)(k0 + kk) * 128u + (uint32_t)s * 32u) >> (ex.gshift + 5)) * 4u);
-      } else {  // groups of 64: scale 2 kb2 + s / 2; a 16-byte load from
-                // 2 k0 + 4 v + s / 2 holds those of kb2 = k0 + 2v, k0 + 2v + 1
-                // in its words 0 and 2
-#pragma unroll
-        for (int v = 0; v < CK2 / 2; ++v) ch.sc4[v] = ld_region16(rsc, so + (uint32_t)(2 * k0 + 4 * v + (s >> 1)) * 4u);
-      }
-#pragma unroll
-      for (int kk = 0; kk < CK2; ++kk) wload(rq, (uint32_t)(k0 + kk), ch.w[kk]);
-    };
-
-    auto bconv = [&](const u32x4 (&w)[WV], int hh) __attribute__((always_inline)) {
-      if constexpr (FMT == kFmtInt4) {
-        const uint32_t w0 = w[0][2 * hh], w1 = w[0][2 * hh + 1];
-        return u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
-      } else {
-        return w[hh];
-      }
-    };
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    bool xseen = false;  // the round's slots are written (all waves)
+    bool xseen = false;  // every wave's slots are written
     auto wait_slots = [&]() __attribute__((always_inline)) {
       if (!xseen) {
         while (__hip_atomic_load(&s_xready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kMW)
@@ -792,137 +864,146 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
         xseen = true;
       }
     };
-    // o[n] of a task from the lane's accumulators: its columns combined, then
-    // the four lanes of the row (k-slots) summed
-    auto row_value = [&](const float (&c)[4]) __attribute__((always_inline)) {
-      float v = __builtin_fmaf(c[1], 256.f, c[0]) + __builtin_fmaf(c[3], 256.f, c[2]) * (1.f / 32768.f);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      return v;
-    };
     uint64_t tmore = 0;  // this wave's tasks (by index) with groups of more than two planes
 
-    auto compute = [&](Chunk& ch, int j) __attribute__((always_inline)) {
-      const int ti = j / CPT, tk = wave + kMW * ti;
-      const int part_i = j % CPT, k0 = part_i * CK2;
-      const int tsk = wuni(s_task[tk]);
-      const int pi = tsk >> 12, tile = tsk & 0xFFF;
-      const int pr = slot_of(pi);
-      const uint8_t* rp = rec + (size_t)pr * NGL * kRecBytes;
-      if (part_i == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = 0.f;
+    // the compute cursor (ct, cp) walks the chunks in the same order
+    int ct = 0, cp = 0;
+    const uint8_t* rp = rec;
+    uint32_t xm0 = 0, xm1 = 0;  // the task's steps with further planes (bit 2 kb2 + hh)
+    auto compute = [&](Chunk& ch) __attribute__((always_inline)) {
+      const int k0 = cp * CK2;
+      const int tp = __builtin_amdgcn_readlane(tk_p, ct);
+      const int slot = (tp >> 16) & 0xFF;
+      if (cp == 0) {
+        rp = rec + (size_t)slot * NGL * kRecBytes;
+        a01 = a23 = 0.f;
         // steps of this task with further planes: bit 2 kb2 + hh for a
         // group G = 8 kb2 + 2 s + hh with P > 2
         xm0 = xm1 = 0;
         for (int g0 = 0; g0 < NG; g0 += 64) {
           const int g = g0 + lane;
           const bool f = g < NG && (*reinterpret_cast<const int*>(rp + (size_t)g * kRecBytes + 84) & 0xFF) > 2;
-          const uint64_t m = __ballot(f);
-          if (m != 0) {
-#pragma unroll
-            for (int bk = 0; bk < 8; ++bk) {  // lanes 8 bk .. 8 bk + 7: groups of k block g0 / 8 + bk
-              const uint32_t mb = (uint32_t)(m >> (8 * bk)) & 0xFFu;
-              const int step = 2 * (g0 / 8 + bk);
-              const uint32_t bits = ((mb & 0x55u) ? 1u : 0u) | ((mb & 0xAAu) ? 2u : 0u);
-              if (step < 32) xm0 |= bits << step;
-              else xm1 |= bits << (step - 32);
-            }
-          }
+          const uint32_t bits = step_bits(__ballot(f));
+          if (g0 < 128) xm0 |= bits << (g0 / 4);
+          else xm1 |= bits << (g0 / 4 - 32);
         }
-        if ((xm0 | xm1) != 0) tmore |= 1ull << ti;
+        if ((xm0 | xm1) != 0) tmore |= 1ull << ct;
       }
-      const uint32_t xm = (uint32_t)((((uint64_t)xm1 << 32) | xm0) >> (2 * k0)) & ((1u << (2 * CK2)) - 1u);
-      if (xm != 0) wait_slots();
+      const uint32_t xm = (uint32_t)((((uint64_t)xm1 << 32) | xm0) >> (2 * k0)) & ((1u << NS) - 1u);
       // scales of the chunk taken here (all words of their loads in use)
       if constexpr (SM == 2)
 #pragma unroll
-        for (int v = 0; v < CK2 / 2; ++v) asm volatile("" : "+v"(ch.sc4[v]));
+        for (int v = 0; v < (CK2 + 1) / 2; ++v) asm volatile("" : "+v"(ch.sc4[v]));
       auto scale_of = [&](int kk) __attribute__((always_inline)) {
         return SM == 2 ? __uint_as_float(ch.sc4[kk / 2][2 * (kk & 1)]) : (SM == 0 ? 1.f : ch.sc[kk]);
       };
-      const bool diag = (n >> 2) == s;
-      // software pipeline over the 2 CK2 steps: the LDS reads of step st + 1
-      // are issued before the matrix instruction of step st, whose result is
-      // taken after that of step st + 1 is issued (same summation order)
+      // the lane's records: step st (k block k0 + st / 2, half st % 2) at
+      // a fixed offset from lb; lanes off the diagonal read the zero block
+      const uint8_t* lb = rp + (size_t)(8 * k0 + 2 * s) * kRecBytes;
+      const uint8_t* ab = diag ? lb + 16 * (n & 3) : zblk;
       struct StepIn {
         u32x4 av, cin;
         float hf;
-        int pinfo;
       };
       auto rd = [&](int st_) __attribute__((always_inline)) {
-        const int G = 8 * (k0 + (st_ >> 1)) + 2 * s + (st_ & 1);
-        const uint8_t* rg = rp + (size_t)G * kRecBytes;
+        const int off = (8 * (st_ >> 1) + (st_ & 1)) * kRecBytes;
         StepIn r;
-        r.av = *reinterpret_cast<const u32x4*>(diag ? rg + 16 * (n & 3) : zrec);
-        r.cin = *reinterpret_cast<const u32x4*>(rg + 64);
-        const uint2 hp = *reinterpret_cast<const uint2*>(rg + 80);
-        r.hf = __uint_as_float(hp.x);
-        r.pinfo = (int)hp.y;
+        r.av = *reinterpret_cast<const u32x4*>(ab + off);
+        r.cin = *reinterpret_cast<const u32x4*>(lb + off + 64);
+        r.hf = *reinterpret_cast<const float*>(lb + off + 80);
         return r;
       };
-      StepIn cur = rd(0);
-      v4i cp = {0, 0, 0, 0};
-      float fp = 0.f;
+      if (xm == 0) {
+        // software pipeline: the LDS reads of step st + 1 are issued before
+        // the matrix instruction of step st, whose result is taken after that
+        // of step st + 1 is issued
+        StepIn cur = rd(0);
+        v4i cprev = {0, 0, 0, 0};
+        float fprev = 0.f;
 #pragma unroll
-      for (int st_ = 0; st_ < 2 * CK2; ++st_) {
-        StepIn nx = cur;
-        if (st_ + 1 < 2 * CK2) nx = rd(st_ + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const u32x4 bw = bconv(ch.w[st_ >> 1], st_ & 1);
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, cur.av), __builtin_bit_cast(v4i, bw),
-                                                            __builtin_bit_cast(v4i, cur.cin), 0, 0, 0);
-        const float f = scale_of(st_ >> 1) * cur.hf;
-        if (st_ > 0)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)cp[i], fp, acc[i]);
-        if ((xm >> st_) & 1) {
-          // plane pair 1 of the step's groups that have a slot (zero record
-          // for the others: they are added after the chunks)
-          const int slot = (cur.pinfo >> 8) - 1;
-          const bool has = (cur.pinfo & 0xFF) > 2 && slot >= 0;
-          const uint8_t* xg = has ? xrec + (size_t)slot * kRecBytes : zrec;
-          const u32x4 xa = *reinterpret_cast<const u32x4*>(diag ? xg + 16 * (n & 3) : zrec);
-          const u32x4 xc = *reinterpret_cast<const u32x4*>(xg + 64);
-          const float xh = *reinterpret_cast<const float*>(xg + 80);
-          const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa), __builtin_bit_cast(v4i, bw),
-                                                               __builtin_bit_cast(v4i, xc), 0, 0, 0);
-          const float f2 = scale_of(st_ >> 1) * xh;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)c2[i], f2, acc[i]);
+        for (int st_ = 0; st_ < NS; ++st_) {
+          StepIn nx = cur;
+          if (st_ + 1 < NS) nx = rd(st_ + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const v4i c = mfma(cur.av, bconv(ch.w[st_ >> 1], st_ & 1), cur.cin);
+          const float f = scale_of(st_ >> 1) * cur.hf;
+          if (st_ > 0) accum(cprev, fprev);
+          __builtin_amdgcn_sched_barrier(0);
+          cprev = c;
+          fprev = f;
+          cur = nx;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        cp = c;
-        fp = f;
-        cur = nx;
-      }
+        accum(cprev, fprev);
+      } else {
+        // with plane pair 1: each step's slot record (or the zero record)
+        // from the step table, read with the step's own records
+        wait_slots();
+        const u32x4 xt = *reinterpret_cast<const u32x4*>(xtab + (((size_t)slot * CPT + cp) * 4 + s) * 8);
+        struct XIn {
+          u32x4 av, cin;
+          float hf;
+        };
+        auto xrd = [&](int st_) __attribute__((always_inline)) {
+          const uint32_t sl = (xt[st_ >> 1] >> (16 * (st_ & 1))) & 0xFFFFu;
+          const uint8_t* xg = xrec + sl * (uint32_t)kRecBytes;
+          XIn r;
+          r.av = *reinterpret_cast<const u32x4*>(diag ? xg + 16 * (n & 3) : zblk);
+          r.cin = *reinterpret_cast<const u32x4*>(xg + 64);
+          r.hf = *reinterpret_cast<const float*>(xg + 80);
+          return r;
+        };
+        StepIn cur = rd(0);
+        XIn xcur = xrd(0);
+        v4i cprev = {0, 0, 0, 0}, xprev = {0, 0, 0, 0};
+        float fprev = 0.f, xfprev = 0.f;
+        bool xhas = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)cp[i], fp, acc[i]);
-      if (part_i == CPT - 1) {
-        const float v = row_value(acc);
-        const int row = 16 * tile + n;
-        const int pair = wuni(R.upair[pi]);
-        if (s == 0 && row < nr) part[(size_t)row * np + pair] = SM == 0 ? v * ch.sc[0] : v;
+        for (int st_ = 0; st_ < NS; ++st_) {
+          StepIn nx = cur;
+          XIn xnx = xcur;
+          if (st_ + 1 < NS) {
+            nx = rd(st_ + 1);
+            xnx = xrd(st_ + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4 bw = bconv(ch.w[st_ >> 1], st_ & 1);
+          const float sc = scale_of(st_ >> 1);
+          const v4i c = mfma(cur.av, bw, cur.cin);
+          const bool xs = (xm >> st_) & 1;
+          v4i cx = {0, 0, 0, 0};
+          if (xs) cx = mfma(xcur.av, bw, xcur.cin);
+          if (st_ > 0) accum(cprev, fprev);
+          if (xhas) accum(xprev, xfprev);
+          __builtin_amdgcn_sched_barrier(0);
+          cprev = c;
+          fprev = sc * cur.hf;
+          xprev = cx;
+          xfprev = sc * xcur.hf;
+          xhas = xs;
+          cur = nx;
+          xcur = xnx;
+        }
+        accum(cprev, fprev);
+        if (xhas) accum(xprev, xfprev);
+      }
+      if (cp == CPT - 1) {
+        const float v = row_value(a01, a23);
+        const int row = 16 * (tp & 0xFFFF) + n;
+        if (s == 0 && row < nr) part[(size_t)row * np + (tp >> 24)] = SM == 0 ? v * ch.sc[0] : v;
+      }
+      if (++cp == CPT) {
+        cp = 0;
+        ++ct;
       }
     };
 
-    load(A, 0);
-    load(B, 1);
-    // the thread's plane pair 1 records into their slots, then this wave is
-    // counted as done (its weights were requested first)
+    for (int j = 0; j < nj; j += kNB) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (xslot[j] >= 0) {
-#pragma unroll
-        for (int k = 0; k < 6; ++k) reinterpret_cast<u32x4*>(xrec + (size_t)xslot[j] * kRecBytes)[k] = xr[j][k];
+      for (int b = 0; b < kNB; ++b) {
+        if (j + b >= nj) break;
+        compute(ring[b]);
+        load(ring[b]);
       }
-    if (lane == 0) __hip_atomic_fetch_add(&s_xready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int j = 0; j < nj; j += 2) {
-      compute(A, j);
-      load(A, j + 2);
-      if (j + 1 >= nj) break;
-      compute(B, j + 1);
-      load(B, j + 3);
     }
 
     // planes past the slots: plane pairs 2 and up, and plane pair 1 of groups
@@ -931,44 +1012,35 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
       wait_slots();
       for (int ti = 0; ti < myt; ++ti) {
         if (((tmore >> ti) & 1) == 0) continue;
-        const int tsk = wuni(s_task[wave + kMW * ti]);
-        const int pi = tsk >> 12, tile = tsk & 0xFFF;
-        const int pair = wuni(R.upair[pi]);
-        const uint8_t* rp = rec + (size_t)slot_of(pi) * NGL * kRecBytes;
+        const int tp = __builtin_amdgcn_readlane(tk_p, ti);
+        const int pair = tp >> 24, tile = tp & 0xFFFF;
+        const uint8_t* trp = rec + (size_t)((tp >> 16) & 0xFF) * NGL * kRecBytes;
         uint32_t tm0 = 0, tm1 = 0;
         for (int g0 = 0; g0 < NG; g0 += 64) {
           const int g = g0 + lane;
-          const int pinfo = g < NG ? *reinterpret_cast<const int*>(rp + (size_t)g * kRecBytes + 84) : 0;
+          const int pinfo = g < NG ? *reinterpret_cast<const int*>(trp + (size_t)g * kRecBytes + 84) : 0;
           const int pc = pinfo & 0xFF;
-          const uint64_t m = __ballot(pc > 4 || (pc > 2 && (pinfo >> 8) == 0));
-          for (int bk = 0; bk < 8; ++bk) {
-            const uint32_t mb = (uint32_t)(m >> (8 * bk)) & 0xFFu;
-            const int step = 2 * (g0 / 8 + bk);
-            const uint32_t bits = ((mb & 0x55u) ? 1u : 0u) | ((mb & 0xAAu) ? 2u : 0u);
-            if (step < 32) tm0 |= bits << step;
-            else tm1 |= bits << (step - 32);
-          }
+          const uint32_t bits = step_bits(__ballot(pc > 4 || (pc > 2 && (pinfo >> 8) == 0)));
+          if (g0 < 128) tm0 |= bits << (g0 / 4);
+          else tm1 |= bits << (g0 / 4 - 32);
         }
         uint64_t tm = ((uint64_t)tm1 << 32) | tm0;
         if (tm == 0) continue;
-        __amdgpu_buffer_rsrc_t rq, rsc;
-        task_rsrc(true, tsk, rq, rsc);
-        const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
-        float tacc[4] = {0.f, 0.f, 0.f, 0.f};
-        const bool diag = (n >> 2) == s;
+        task_rsrc(ti);
+        float t01 = 0.f, t23 = 0.f;
         while (tm != 0) {
           const int b = __builtin_ctzll(tm);
           tm &= tm - 1;
           const uint32_t kb2 = (uint32_t)(b >> 1);
           const int hh = b & 1;
           u32x4 w[WV];
-          wload(rq, kb2, w);
+          wload(kb2, w);
           float sc = 1.f;
           if constexpr (SM == 1) sc = ld_region4(rsc, so + ((kb2 * 128u + (uint32_t)s * 32u) >> (ex.gshift + 5)) * 4u);
           if constexpr (SM == 2) sc = ld_region4(rsc, so + (2u * kb2 + (uint32_t)(s >> 1)) * 4u);
           const u32x4 bw = bconv(w, hh);
           const int G = 8 * (int)kb2 + 2 * s + hh;
-          const int pinfo = *reinterpret_cast<const int*>(rp + (size_t)G * kRecBytes + 84);
+          const int pinfo = *reinterpret_cast<const int*>(trp + (size_t)G * kRecBytes + 84);
           const int pc = pinfo & 0xFF;
           const int qlo = (pinfo >> 8) != 0 ? 2 : 1;
           int nq = (pc + 1) / 2;
@@ -980,14 +1052,12 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
             const u32x4 xa = __builtin_amdgcn_raw_buffer_load_b128(rall, diag ? ro + 16u * (uint32_t)(n & 3) : kOutside, 0, 0);
             const u32x4 xc = __builtin_amdgcn_raw_buffer_load_b128(rall, ro + 64u, 0, 0);
             const float xh = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rall, ro + 80u, 0, 0));
-            const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa), __builtin_bit_cast(v4i, bw),
-                                                                 __builtin_bit_cast(v4i, xc), 0, 0, 0);
-            const float f2 = sc * xh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tacc[i] = __builtin_fmaf((float)c2[i], f2, tacc[i]);
+            const v4i c2 = mfma(xa, bw, xc);
+            t01 = __builtin_fmaf((float)(c2[0] + (c2[1] << 8)), sc * xh, t01);
+            t23 = __builtin_fmaf((float)(c2[2] + (c2[3] << 8)), sc * xh, t23);
           }
         }
-        float v = row_value(tacc);
+        float v = row_value(t01, t23);
         if constexpr (SM == 0) v *= ld_region4(rsc, so);
         const int row = 16 * tile + n;
         if (s == 0 && row < nr) part[(size_t)row * np + pair] += v;
@@ -996,6 +1066,7 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
     pb = pe;
     ub = ue;
     if (pb < nvalid && ub < nu && R.ustart[ub] > pb) --ub;  // an expert split over rounds continues
+    first = false;
   }
   __syncthreads();
   // y_t[r] = sum over valid slots j, in order, of w_tj * part[r][t k + j]
@@ -1080,11 +1151,14 @@ bool dn_plan(int fmt, int T, int topk, int H, int I, int cus, DnPlan& p) {
   p.Rb = (H + cus - 1) / cus;
   p.blocks = (H + p.Rb - 1) / p.Rb;  // every workgroup has rows
   const int np = T * topk;
-  if ((p.Rb + 15) / 16 > 4096 || (I + 127) / 128 > 32) return false;  // task and step bit fields
-  const size_t fixed = ((size_t)p.Rb * np * 4 + 15) / 16 * 16 + kRecBytes;  // part, zero record
-  const size_t per_pair = (size_t)dn_ngl(fmt, I) * kRecBytes;
+  const int ntile = (p.Rb + 15) / 16;
+  if (ntile > kMaxTasksPerWave * kMW || ntile > 0xFFFF || (I + 127) / 128 > 32) return false;  // bit masks, fields
+  const int cpt = ((I + 127) / 128 + dn_ck2(fmt) - 1) / dn_ck2(fmt);
+  const size_t fixed = ((size_t)p.Rb * np * 4 + 15) / 16 * 16 + dn_zblock(fmt) + kRecBytes;  // part, zeros
+  const size_t per_pair = (size_t)dn_ngl(fmt, I) * kRecBytes + (size_t)cpt * 4 * 16;          // records, step table
   if (fixed + per_pair > kDnLdsMax) return false;
   p.PR = (int)std::min<size_t>((size_t)np, (kDnLdsMax - fixed) / per_pair);  // pairs per round
+  p.PR = std::min(p.PR, kMaxTasksPerWave * kMW / ntile);                      // tasks per wave: one per lane
   const size_t used = fixed + (size_t)p.PR * per_pair;
   p.xcap = (int)std::min<size_t>(2 * kMT, (kDnLdsMax - used) / kRecBytes);
   p.lds = used + (size_t)p.xcap * kRecBytes;

@@ -111,10 +111,32 @@ def zipf_routing(g, n_tokens, n_experts, top_k, alpha=1.1):
     return ids.astype(np.int32), w.astype(np.float32)
 
 
-def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None, threads=1):
+# standard deviation of a uniformly drawn code, as the dequantized value
+# (code - offset): int4 nibble - 8, int8 in [-127, 127], int3 code - 4
+_CODE_STD = {FMT_INT4: float(np.sqrt((16 * 16 - 1) / 12.0)), FMT_INT8_ROW: float(np.sqrt((255 * 255 - 1) / 12.0)),
+             FMT_INT3: float(np.sqrt((8 * 8 - 1) / 12.0))}
+
+
+def scale_range(fmt, k, scales):
+    """Scale draw range of an n x k matrix.  "wide": U(0.005, 0.02) whatever
+    the shape (with N(0, 1) activations the gate/up pre-activations then have
+    a standard deviation of about 4.7 at k = 6144, and SiLU's negative tail
+    spreads h over many binades); "unit": U(0.5, 1.5) / (code std sqrt(k)),
+    so that a product with N(0, 1) inputs has about unit variance, as the
+    normalised layers of a trained model keep them."""
+    if scales == "wide":
+        return 0.005, 0.02
+    if scales == "unit":
+        c = 1.0 / (_CODE_STD[fmt] * np.sqrt(k))
+        return 0.5 * c, 1.5 * c
+    raise ValueError(scales)
+
+
+def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None, threads=1, scales="wide"):
     """Stacked expert weights as a dict (the layout the library and the oracle
     both take).  `experts` limits generation to a subset of ids; the other
-    experts' slots are left zero (only valid when routing avoids them)."""
+    experts' slots are left zero (only valid when routing avoids them).
+    `scales`: the scale draw range, see scale_range."""
     G_h = n_groups(hidden, gs) if fmt == FMT_INT4 else 1
     G_i = n_groups(inter, gs) if fmt == FMT_INT4 else 1
     rb_h = hidden // 2 if fmt == FMT_INT4 else hidden
@@ -135,7 +157,7 @@ def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None, threads=1)
     def fill(e):
         for tag, name, n, k in ((_T_GATE, "gate", inter, hidden), (_T_UP, "up", inter, hidden),
                                 (_T_DOWN, "down", hidden, inter)):
-            q, s = quant_matrix(rng(seed, tag, e), fmt, n, k, gs)
+            q, s = quant_matrix(rng(seed, tag, e), fmt, n, k, gs, *scale_range(fmt, k, scales))
             out[name + "_q"][e] = q
             out[name + "_s"][e] = s.reshape(out[name + "_s"][e].shape)
 
