@@ -305,16 +305,20 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
   // any weights (loads complete in order: staging x then waits for x alone)
   const int id_t = threadIdx.x < T * a.topk ? a.ids[threadIdx.x] : -1;
   constexpr int NV = XT == kBF16 ? PER / 8 : PER / 4;  // 16-byte words of a group
+  // (buffer loads: a generic load would make its first use wait for every
+  // load issued after it, the weights included)
   u32x4 raw[2][NV];
+  {
+    const __amdgpu_buffer_rsrc_t rx = region_rsrc(a.x, (uint32_t)((size_t)T * H * (XT == kBF16 ? 2 : 4)));
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int it = threadIdx.x + q2 * kGT;
-    const int t = min(it / KCHP, T - 1), c = it - (it / KCHP) * KCHP;
-    const bool real = it < T * KCHP && c < KCH;
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) +
-                                                      ((int64_t)t * H + (int64_t)(real ? c : 0) * PER) * (XT == kBF16 ? 2 : 4));
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int it = threadIdx.x + q2 * kGT;
+      const int t = min(it / KCHP, T - 1), c = it - (it / KCHP) * KCHP;
+      const bool real = it < T * KCHP && c < KCH;
+      const uint32_t off = (uint32_t)(((int64_t)t * H + (int64_t)(real ? c : 0) * PER) * (XT == kBF16 ? 2 : 4));
 #pragma unroll
-    for (int q = 0; q < NV; ++q) raw[q2][q] = src[q];
+      for (int q = 0; q < NV; ++q) raw[q2][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u * q, 0, 0);
+    }
   }
   build_route(id_t, 0.f, T * a.topk, ex.E, R);
   const int nu = R.nu;
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
 // output is y_t = sum_j w_tj o_tj in slot order, so y does not depend on
 // timing.
 constexpr int kMaxTasksPerWave = 64;            // tasks of a wave in one round (one per lane)
-constexpr int kNB = 4;                          // chunks in flight per wave
+constexpr int kNB = 2;                          // chunks in flight per wave
 constexpr uint32_t kOutside = 0x80000000u;      // a buffer offset past every record: loads zeros
 constexpr size_t kDnLdsMax = 144 * 1024;        // dynamic LDS of the down kernel
 
@@ -653,6 +657,8 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
 
   // staged items: (pair slot, group) records, 96 bytes (zero past I / 16)
   const bool one = np <= PR;
+  // (buffer loads: a generic load would make its first use wait for every
+  // load issued after it)
   u32x4 st[2][6];
   auto stage_load = [&](int nit, int pb_, bool routed) __attribute__((always_inline)) {
 #pragma unroll
@@ -660,10 +666,9 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
       const int it = min((int)threadIdx.x + kMT * j, max(nit, 1) - 1);
       const int pr = it / NGL, g = it - pr * NGL;
       const int pair = (one || !routed) ? pr : R.upair[pb_ + pr];
-      const u32x4* src =
-          reinterpret_cast<const u32x4*>(a.hrec + ((int64_t)pair * kRecPairs * NGP + min(g, NG - 1)) * kRecBytes);
+      const uint32_t off = (uint32_t)(((int64_t)pair * kRecPairs * NGP + min(g, NG - 1)) * kRecBytes);
 #pragma unroll
-      for (int k = 0; k < 6; ++k) st[j][k] = src[k];
+      for (int k = 0; k < 6; ++k) st[j][k] = __builtin_amdgcn_raw_buffer_load_b128(rall, off + 16u * k, 0, 0);
     }
   };
   auto put = [&](int it, const u32x4* v6) __attribute__((always_inline)) {
