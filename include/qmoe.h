@@ -256,6 +256,32 @@ QM_API int moe_expert_ffn_noalloc(const qm_experts *ex, const void *x, int32_t x
 /* Static text for a qm_status value. */
 QM_API const char *qm_strerror(int status);
 
+/* ---- packing, validation and quantization (host memory, no GPU) ----------
+ * Weights in the layouts above, made on the host before the upload [Q:
+ * int4-gs64 arriving as fmt 4 / group 64 at half a byte per element; V:
+ * fmt=4 grouped scales].  All buffers are host memory owned by the caller;
+ * nothing is allocated; QM_ERR_INVALID (nothing written) for a null pointer,
+ * n < 0, k <= 0 or a value the format cannot hold.
+ *
+ * qm_pack_int4: v [n][k] int8 values in [-8, 7] (row-major) -> q [n][k/2]
+ *   bytes, nibble = v + 8, even element in the low nibble.  k must be even.
+ * qm_pack_int8: v [n][k] -> q [n][k] (the values themselves; q may be v).
+ * qm_validate: checks a format's shape rules and that its scales
+ *   ([n][groups] fp32, groups as in "Weight formats") are all finite; any
+ *   int4/int8/int3 code byte is valid, so the codes are not read.
+ * qm_quantize_int4: fp32 w [n][k] -> q [n][k/2] and scales [n][k/gs]
+ *   (group_size 0 or k: [n]): per group s = max|w| / 7, code = clamp(
+ *   round-half-even(w / s), -8, 7) (all codes 0 where s = 0).  w must be finite.
+ * qm_quantize_int8: fp32 w [n][k] -> q [n][k], scales [n]: per row s =
+ *   max|w| / 127, code = clamp(round-half-even(w / s), -127, 127).
+ * (The quantizers are one plain rounding scheme; the kernels take any codes
+ * and scales.) */
+QM_API int qm_pack_int4(const int8_t *v, int64_t n, int64_t k, uint8_t *q);
+QM_API int qm_pack_int8(const int8_t *v, int64_t n, int64_t k, int8_t *q);
+QM_API int qm_validate(int32_t fmt, int64_t n, int64_t k, int32_t group_size, const float *scales);
+QM_API int qm_quantize_int4(const float *w, int64_t n, int64_t k, int32_t group_size, uint8_t *q, float *scales);
+QM_API int qm_quantize_int8(const float *w, int64_t n, int64_t k, int8_t *q, float *scales);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,14 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def host_sources():
+    """Host-only C++ (packing and validation): built with g++."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
 # The sources the decode kernels are built from (the fused gate+up kernel
 # whose counters the bench reports, and the down kernel).
 DECODE_SOURCES = ("device.hpp", "launch.hpp", "planes.hpp", "moe_decode.hip", "qmoe.hip")
@@ -55,8 +63,11 @@ def source_digest(names=None):
 
 
 def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", "-o", obj, src]
+    obj = os.path.join(BUILD, os.path.basename(src).rsplit(".", 1)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = ["g++", *HOST_FLAGS, *extra, "-c", "-o", obj, src]
+    else:
+        cmd = [HIPCC, *FLAGS, *extra, "-c", "-o", obj, src]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops' is not a recognized" not in l]
     if r.returncode:
@@ -66,10 +77,10 @@ def _compile(src, extra):
 
 def build(out=LIB, verbose=False, extra=(), jobs=None):
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + host_sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+        results = list(ex.map(lambda s: _compile(s, list(extra) if not s.endswith(".cpp") else []), srcs))
     for obj, msgs in results:
         if verbose and msgs:
             print("\n".join(msgs))

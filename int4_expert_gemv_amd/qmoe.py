@@ -21,7 +21,9 @@ QM_NOALLOC_SCRATCH_BYTES = 32 << 20
 QM_PATH_AUTO, QM_PATH_DECODE, QM_PATH_PREFILL = 0, 1, 2
 
 EXPORTS = ("qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_ffn_path",
-           "moe_gate_up", "moe_down", "moe_expert_ffn_noalloc", "qm_strerror")
+           "moe_gate_up", "moe_down", "moe_expert_ffn_noalloc", "qm_strerror",
+           "qm_pack_int4", "qm_pack_int8", "qm_validate", "qm_quantize_int4", "qm_quantize_int8")
+QM_FMT_INT3 = 5
 
 
 class QmError(RuntimeError):
@@ -70,6 +72,13 @@ def load(path=LIB_PATH):
     L.moe_expert_ffn_noalloc.restype = ctypes.c_int
     L.qm_strerror.argtypes = [ctypes.c_int]
     L.qm_strerror.restype = ctypes.c_char_p
+    L.qm_pack_int4.argtypes = [vp, i64, i64, vp]
+    L.qm_pack_int8.argtypes = [vp, i64, i64, vp]
+    L.qm_validate.argtypes = [i32, i64, i64, i32, vp]
+    L.qm_quantize_int4.argtypes = [vp, i64, i64, i32, vp, vp]
+    L.qm_quantize_int8.argtypes = [vp, i64, i64, vp, vp]
+    for f in (L.qm_pack_int4, L.qm_pack_int8, L.qm_validate, L.qm_quantize_int4, L.qm_quantize_int8):
+        f.restype = ctypes.c_int
     return L
 
 
@@ -180,3 +189,62 @@ def raw_status(fn, *args):
     """Call an entry point with raw ctypes arguments and return its status
     (used by the host-side validation tests)."""
     return getattr(lib, fn)(*args)
+
+
+# ---- host packing (numpy arrays in host memory; no GPU) -----------------------------
+
+def _host(a, dtype):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (np.dtype(dtype), a.dtype))
+    return a
+
+
+def pack_int4(v):
+    """int8 values in [-8, 7], shape [n][k] -> packed uint8 [n][k/2]."""
+    import numpy as np
+    v = _host(v, np.int8)
+    n, k = v.shape
+    q = np.empty((n, k // 2), np.uint8)
+    _check(lib.qm_pack_int4(v.ctypes.data, n, k, q.ctypes.data))
+    return q
+
+
+def pack_int8(v):
+    """int8 values [n][k] -> the int8 layout [n][k]."""
+    import numpy as np
+    v = _host(v, np.int8)
+    q = np.empty_like(v)
+    _check(lib.qm_pack_int8(v.ctypes.data, v.shape[0], v.shape[1], q.ctypes.data))
+    return q
+
+
+def validate(fmt, n, k, group_size, scales):
+    """QM_OK when the format's shape rules hold and every scale is finite."""
+    import numpy as np
+    s = _host(scales, np.float32)
+    return lib.qm_validate(fmt, n, k, group_size, s.ctypes.data)
+
+
+def quantize_int4(w, group_size):
+    """fp32 [n][k] -> (packed uint8 [n][k/2], fp32 scales [n][groups])."""
+    import numpy as np
+    w = _host(w, np.float32)
+    n, k = w.shape
+    groups = 1 if group_size in (0, k) else k // group_size
+    q = np.empty((n, k // 2), np.uint8)
+    s = np.empty((n, groups), np.float32)
+    _check(lib.qm_quantize_int4(w.ctypes.data, n, k, group_size, q.ctypes.data, s.ctypes.data))
+    return q, s
+
+
+def quantize_int8(w):
+    """fp32 [n][k] -> (int8 [n][k], fp32 scales [n][1])."""
+    import numpy as np
+    w = _host(w, np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), np.int8)
+    s = np.empty((n, 1), np.float32)
+    _check(lib.qm_quantize_int8(w.ctypes.data, n, k, q.ctypes.data, s.ctypes.data))
+    return q, s

@@ -35,7 +35,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     assert set(names) == {"qgemv", "qgemv_pair", "qgemv_norm_chain", "qgemm_small", "moe_expert_ffn_workspace", "moe_expert_ffn",
                           "moe_expert_ffn_path", "moe_gate_up", "moe_down", "moe_expert_ffn_noalloc",
-                          "qm_strerror"}
+                          "qm_strerror", "qm_pack_int4", "qm_pack_int8", "qm_validate", "qm_quantize_int4",
+                          "qm_quantize_int8"}
 
 
 def test_library_exports_every_declared_symbol(q):
