@@ -11,7 +11,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqmoe.so")
+# QMOE_LIB_PATH names another build of the same sources (e.g. a sanitized host build)
+LIB_PATH = os.environ.get("QMOE_LIB_PATH", os.path.join(HERE, "libqmoe.so"))
 
 QM_OK, QM_ERR_INVALID, QM_ERR_UNSUPPORTED, QM_ERR_WORKSPACE, QM_ERR_LAUNCH, QM_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 QM_FMT_INT8_ROW, QM_FMT_INT4 = 1, 4

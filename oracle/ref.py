@@ -183,10 +183,11 @@ _default = None
 
 
 def oracle():
-    """The shared oracle instance (builds the library on first use if absent)."""
+    """The shared oracle instance (builds the library on first use if absent;
+    QMREF_LIB names another build of the same source, e.g. a sanitized one)."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("QMREF_LIB", LIB))
     return _default
 
 

@@ -15,7 +15,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmoe.h")
-LIB = os.path.join(ROOT, "int4_expert_gemv_amd", "libqmoe.so")
+LIB = os.environ.get("QMOE_LIB_PATH", os.path.join(ROOT, "int4_expert_gemv_amd", "libqmoe.so"))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libqmoe.so not built")
 
