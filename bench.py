@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--scales", default="unit", choices=["unit", "wide"],
+                   help="expert weight scale draws: 'unit' gives unit-variance gate/up pre-activations (as a trained "
+                        "model's normalised layers do), 'wide' the fixed U(0.005, 0.02) range of the tests")
     p.add_argument("--graph", action="store_true",
                    help="gemv / qprep: time the calls as one HIP graph replay (no per-call host launch cost) "
                         "instead of back-to-back launches from Python")
@@ -98,16 +101,108 @@ def counter_traffic(name):
 
 
 def routing_schedule(seed, n_steps, T, E, k):
-    """Per step: T tokens' top-k ids (distinct within a token) taken from a
-    walk over random permutations of the experts, and softmax gate weights."""
+    """Per step: T tokens' top-k ids (distinct within a token) and softmax
+    gate weights.  One token: a walk over random permutations of the experts
+    (an expert comes back only after all others, so no step finds its weights
+    in the last-level cache).  Several tokens: every token draws its k experts
+    independently (uniformly, without replacement within the token), so
+    tokens share experts as independent routing does (about 58.7 distinct
+    experts of 320 for 8 tokens of top-8)."""
     g = np.random.default_rng([seed, 1234])
-    need = n_steps * T * k
-    perm = np.concatenate([g.permutation(E) for _ in range(need // E + 2)])
-    ids = perm[:need].reshape(n_steps, T, k).astype(np.int32)
+    if T == 1:
+        need = n_steps * k
+        perm = np.concatenate([g.permutation(E) for _ in range(need // E + 2)])
+        ids = perm[:need].reshape(n_steps, 1, k).astype(np.int32)
+    else:
+        ids = np.stack([np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+                        for _ in range(n_steps)]).astype(np.int32)
     logits = g.standard_normal(size=(n_steps, T, k))
     w = np.exp(logits - logits.max(axis=2, keepdims=True))
     w = (w / w.sum(axis=2, keepdims=True)).astype(np.float32)
     return ids, w
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(o, run, units_per_call, unit_bytes, seconds, what):
+    """The oracle as it stands, timed on the host: run(i) is one call over
+    sample i (units_per_call of the metric's units each, unit_bytes bytes per
+    unit); first with every host thread (OpenMP over rows), then on one
+    thread, each for about `seconds` (at least one call)."""
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+    for label, nthr in (("multi", threads), ("single", 1)):
+        o.set_threads(nthr)
+        t0 = time.time()
+        done = 0
+        while done == 0 or (time.time() - t0) < seconds:
+            run(done)
+            done += 1
+        el = time.time() - t0
+        out[label] = (done, el, nthr)
+    o.set_threads(threads)
+    (dm, em, tm), (ds, es, _) = out["multi"], out["single"]
+    gbs = lambda d, e: round(d * units_per_call * unit_bytes / e / 1e9, 4)
+    return {"value": gbs(dm, em), "unit": "GB/s", "cores": tm, "kind": "oracle",
+            "sample": "%s: %d calls on %d threads, %.2f ms per call" % (what, dm, tm, 1e3 * em / dm),
+            "single_thread": {"value": gbs(ds, es), "unit": "GB/s", "cores": 1,
+                              "sample": "%s: %d calls on 1 thread, %.2f ms per call" % (what, ds, 1e3 * es / ds)},
+            "cpu_model": cpu_model()}
+
+
+def stream_read_gbs():
+    """A measured streaming-read rate of this GPU: torch's row sums over a
+    2 GiB fp32 tensor viewed as 512 rows of 2^20 (the fastest plain read
+    among torch's reductions here), best of 10; the denominator next to the
+    published peak."""
+    import torch
+    a = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    rows = a.view(-1, 1 << 20)
+    for _ in range(3):
+        rows.sum(dim=1)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rows.sum(dim=1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    nbytes = a.numel() * 4
+    del a, rows
+    return round(nbytes / (best * 1e-3) / 1e9, 1)
+
+
+def stream_fields(achieved):
+    sr = stream_read_gbs()
+    return {"measured_stream_read_gbs": sr, "frac_of_measured_stream": round(achieved / sr, 4)}
+
+
+def per_launch_ms(launch, n):
+    """Average duration of launch(j), j < n, each bracketed by its own pair
+    of events on the launch stream (torch's current stream): the kernel's
+    own time plus the event granularity, without the gaps between calls."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for j in range(n):
+        ev[j][0].record()
+        launch(j)
+        ev[j][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def bench_moe(args, E, H, I):
@@ -120,7 +215,7 @@ def bench_moe(args, E, H, I):
     n_steps = args.warmup + args.steps
     print("generating %d experts (hidden %d, inter %d, int4 gs=%d)" % (E + nsh, H, I, gs), file=sys.stderr, flush=True)
     t0 = time.time()
-    ex = synth.expert_set(args.seed, fmt, E + nsh, H, I, gs, threads=min(16, os.cpu_count() or 4))
+    ex = synth.expert_set(args.seed, fmt, E + nsh, H, I, gs, threads=min(16, os.cpu_count() or 4), scales=args.scales)
     d = {key: dev(ex[key]) for key in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}
     torch.cuda.synchronize()
     print("generated+uploaded in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
@@ -177,16 +272,10 @@ def bench_moe(args, E, H, I):
             step(j)
         torch.cuda.synchronize()
 
-    # dominant kernel: the fused gate+up+SiLU stage launched back to back over
-    # the same routing draws (events on the launch stream around the launches)
-    gs0, gs1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    gs0.record()
-    for j in range(args.steps):
-        qmoe.moe_gate_up(e, x_d[args.warmup + j], ids_d[args.warmup + j], h, ws)
-    gs1.record()
-    torch.cuda.synchronize()
-    gu_ms = gs0.elapsed_time(gs1) / args.steps
+    # dominant kernel: the fused gate+up+SiLU stage (one launch), over the
+    # same routing draws, each launch bracketed by its own events
+    gu_ms = per_launch_ms(lambda j: qmoe.moe_gate_up(e, x_d[args.warmup + j], ids_d[args.warmup + j], h, ws),
+                          args.steps)
 
     # the two stage entry points on the last step, untimed (the layer call may
     # run them as one launch: then the two agree to fp32 rounding, not bit for bit)
@@ -212,17 +301,10 @@ def bench_moe(args, E, H, I):
 
     cpu = None
     if not args.no_cpu:
-        threads = len(os.sched_getaffinity(0))
-        o.set_threads(threads)
-        t0 = time.time()
-        done = 0
-        while done < n_steps and (time.time() - t0) < args.cpu_seconds:
-            o.moe_ffn(ex, x_h[done], ids_h[done], w_h[done], want_norm=False)
-            done += 1
-        el = time.time() - t0
-        cpu = {"value": round(done * step_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": "%d of the same decode steps (routing draws 0..%d), fp64 oracle, OpenMP over rows; "
-                         "%.2f ms per step" % (done, done - 1, 1e3 * el / max(done, 1))}
+        cpu = cpu_baseline(o, lambda i: o.moe_ffn(ex, x_h[i % n_steps], ids_h[i % n_steps], w_h[i % n_steps],
+                                                  want_norm=False),
+                           1, step_bytes, args.cpu_seconds / 2, "the same decode steps (routing draws 0, 1, ...), "
+                                                                 "fp64 oracle")
 
     gname = "g%d" % gs if gs else "row"
     tag = "%s_%s_t%d%s" % (args.config, gname, T, "_shared" if nsh else "")
@@ -233,16 +315,23 @@ def bench_moe(args, E, H, I):
     return {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_layer": round(ms_step * 1e3, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, %s, %d token(s), "
-                               "int4-%s weights, bf16 x" % (H, E, I, routing, T, gname),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i32+f32",
+        "data": "synthetic (seeded; weight scales '%s')" % args.scales,
+        "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, %s, %d token(s)%s, "
+                               "int4-%s weights, bf16 x" % (H, E, I, routing, T,
+                                                            " routed independently" if T > 1 else "", gname),
                    "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": "int4-" + gname,
-                   "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4)},
+                   "unique_experts_per_step": round(float(np.mean(uniq)), 2),
+                   "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4),
+                   "arithmetic": "integer dot products (int4 x int4 digits, int8 matrix instructions) into int32, "
+                                 "combined in fp32"},
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("moe_gate_up_%s_counters" % tag),
-                     "kernel": "fused gate+up+SiLU (moe_gate_up stage)", "us_per_launch": round(gu_ms * 1e3, 3),
-                     "bytes_per_launch": int(gu_bytes)},
+                     "kernel": "fused gate+up+SiLU (moe_gate_up stage, one launch)",
+                     "us_per_launch": round(gu_ms * 1e3, 3), "bytes_per_launch": int(gu_bytes),
+                     "timing": "each launch between its own pair of HIP events on the launch stream, averaged",
+                     **stream_fields(gu_gbs)},
         "parity": {"max_norm_err": err, "tol": 2e-4, "stage_entry_points_max_norm_err": err_stages,
                    "stage_entry_points_identical": same},
         "cpu_baseline": cpu,
@@ -306,6 +395,17 @@ def bench_prefill(args):
     pick = np.array([0, 1, T // 2, T - 1])
     yr, _, nr = ref.oracle().moe_ffn(ex, xs[j][pick], routes[j][0][pick], routes[j][1][pick], flags=ref.BF16_ACT)
     err = ref.max_norm_err(y.cpu().numpy()[pick], yr, nr)
+    cpu = None
+    if not args.no_cpu:
+        # the oracle on 32 of the step's 512 tokens (a full step takes minutes
+        # on the host), scaled to the step's bytes per token
+        sub = np.arange(32) * (T // 32)
+        o = ref.oracle()
+        cpu = cpu_baseline(o, lambda i: o.moe_ffn(ex, xs[i % draws][sub], routes[i % draws][0][sub],
+                                                  routes[i % draws][1][sub], flags=ref.BF16_ACT, want_norm=False),
+                           32, step_bytes / T, args.cpu_seconds / 2,
+                           "32 tokens (every 16th) of a prefill step, fp64 oracle; bytes counted as the step's "
+                           "bytes per token")
     return {"metric": "achieved HBM GB/s + us/layer for int4-g64 MoE expert FFN prefill (512 tokens)",
             "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms, 5), "us_per_layer": round(ms * 1e3, 2), "higher_is_better": True,
@@ -319,7 +419,7 @@ def bench_prefill(args):
                          "mfma_tflops": round(tflops, 2), "mfma_peak_tflops": MFMA_PEAK,
                          "mfma_utilisation": round(tflops / MFMA_PEAK, 4)},
             "parity": {"max_norm_err": err, "tol": 2e-4, "tokens_checked": pick.tolist()},
-            "cpu_baseline": None}
+            "cpu_baseline": cpu}
 
 
 def graph_ms(fn, steps):
@@ -414,6 +514,14 @@ def bench_gemv(args):
         err = max(err, ref.max_norm_err(y2.cpu().numpy(), yr, nr))
     byts = mb + B * k * 2 + B * (n + n2) * 4
     gbs = byts / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        def cpu_call(i):
+            for b in range(B):
+                o.gemv(fmt, n, k, gs, qw, s, x_h[b], want_norm=False)
+            if n2:
+                o.gemv(fmt, n2, k, gs, qw2, s2, x_h[0], want_norm=False)
+        cpu = cpu_baseline(o, cpu_call, 1, byts, args.cpu_seconds / 2, "the same call, fp64 oracle")
     wname = ("int4-g%d" % gs if gs else "int4-row") if fmt == 4 else ("int3-g64" if fmt == 5 else "int8-row")
     return {"metric": "achieved HBM GB/s for quantized GEMV", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 3),
@@ -424,7 +532,7 @@ def bench_gemv(args):
                        "timing": "HIP graph replay" if args.graph else "back-to-back launches from Python"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,
+            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": cpu,
             **({"separate_calls_us": round(sep_ms * 1e3, 3)} if n2 else {})}
 
 
@@ -491,6 +599,13 @@ def bench_qprep(args):
     err = max(ref.max_norm_err(qo.cpu().numpy(), yq, nrq), ref.max_norm_err(kv.cpu().numpy(), yk, nrk))
     byts = mb + k * 2 + (na + nkv + nq) * 4 + na * 4
     gbs = byts / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        def cpu_call(i):
+            u0, _ = o.gemv(*mats[0][0], x_h, want_norm=False)
+            o.gemv(*mats[1][0], x_h, want_norm=False)
+            o.gemv(*mats[2][0], o.rmsnorm(u0, gw_h, eps), want_norm=False)
+        cpu = cpu_baseline(o, cpu_call, 1, byts, args.cpu_seconds / 2, "the same chain, fp64 oracle")
     return {"metric": "achieved HBM GB/s for the q-prep chain (pair GEMV, RMS norm, GEMV)", "value": round(gbs, 2),
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "us_per_call": round(ms * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -500,7 +615,7 @@ def bench_qprep(args):
                        "timing": "HIP graph replay" if args.graph else "back-to-back launches from Python"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": None,
+            "parity": {"max_norm_err": err, "tol": 2e-4}, "cpu_baseline": cpu,
             "norm_on_host_us": round(host_ms * 1e3, 3)}
 
 

@@ -217,9 +217,10 @@ QM_API int moe_expert_ffn_path(const qm_experts *ex, const void *x, int32_t x_dt
 /* Stage 1 of the decode path on its own (the fused gate+up dispatch of the
  * "qmatmul_gate_up.comp" commit note [V]): for every pair p = t*top_k + j
  * with a valid id e, h[p][:] = silu(G_e x_t) * (U_e x_t).  Rows of pairs with
- * an invalid id are not written.  n_tokens must fit one decode pass (at most
- * QM_DECODE_MAX_TOKENS, fewer for very wide hidden sizes; QM_ERR_UNSUPPORTED
- * otherwise).  h: device fp32 [n_tokens*top_k][inter], 4-byte aligned.
+ * an invalid id are not written.  Any n_tokens, in the decode passes
+ * moe_expert_ffn uses (a few tokens per launch; each expert's weights are
+ * read once per pass for all of that pass's tokens routed to it).
+ * h: device fp32 [n_tokens*top_k][inter], 4-byte aligned.
  * workspace as for moe_expert_ffn (scratch for activations that need more
  * than two digit planes).                                                   */
 QM_API int moe_gate_up(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,

@@ -373,12 +373,17 @@ int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
   const int tpp = dec_tokens(ex, top_k);
-  if (tpp == 0 || n_tokens > tpp) return QM_ERR_UNSUPPORTED;  // one decode pass
+  if (tpp == 0) return QM_ERR_UNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
-  MoeDecArgs a = dec_args(expert_args(ex), x, x_dtype, 0, n_tokens, topk_ids, nullptr, top_k, h, nullptr, workspace);
-  a.hrec = nullptr;  // h only: no records for a down pass
-  const hipError_t err = launch_moe_gate_up2(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
+  // decode passes of up to tpp tokens, as moe_expert_ffn runs them
+  hipError_t err = hipSuccess;
+  for (int t0 = 0; t0 < n_tokens && err == hipSuccess; t0 += tpp) {
+    const int nt = n_tokens - t0 < tpp ? n_tokens - t0 : tpp;
+    MoeDecArgs a = dec_args(expert_args(ex), x, x_dtype, t0, nt, topk_ids, nullptr, top_k, h, nullptr, workspace);
+    a.hrec = nullptr;  // h only: no records for a down pass
+    err = launch_moe_gate_up2(ex->fmt, x_dtype, grouped, a, static_cast<hipStream_t>(stream));
+  }
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }
@@ -397,12 +402,16 @@ int moe_down(const qm_experts* ex, const float* h, int32_t n_tokens, const int32
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
   const int tpp = dec_tokens(ex, top_k);
-  if (tpp == 0 || n_tokens > tpp) return QM_ERR_UNSUPPORTED;  // one decode pass
+  if (tpp == 0) return QM_ERR_UNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
     return QM_ERR_WORKSPACE;
-  const MoeDecArgs a = dec_args(expert_args(ex), nullptr, QM_F32, 0, n_tokens, topk_ids, topk_w, top_k,
-                                const_cast<float*>(h), y, workspace);
-  const hipError_t err = launch_moe_down2(ex->fmt, grouped, a, true, static_cast<hipStream_t>(stream));
+  hipError_t err = hipSuccess;
+  for (int t0 = 0; t0 < n_tokens && err == hipSuccess; t0 += tpp) {
+    const int nt = n_tokens - t0 < tpp ? n_tokens - t0 : tpp;
+    const MoeDecArgs a = dec_args(expert_args(ex), nullptr, QM_F32, t0, nt, topk_ids, topk_w, top_k,
+                                  const_cast<float*>(h), y, workspace);
+    err = launch_moe_down2(ex->fmt, grouped, a, true, static_cast<hipStream_t>(stream));
+  }
   if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
   return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
 }

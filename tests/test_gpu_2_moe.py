@@ -163,6 +163,35 @@ def test_moe_one_token_stages_match_layer(q):
     assert torch.equal(y1, y2)
 
 
+def test_moe_stages_over_several_passes(q, oracle):
+    """8 tokens at hidden 6144 run as two decode passes (the gate+up kernel
+    holds the activations of fewer tokens at a time): the stage calls loop
+    the same passes as the layer call and give the same y bit for bit; every
+    token's experts drawn independently from 24, so tokens share experts."""
+    E, H, I, T, k = 24, 6144, 2048, 8, 8
+    print("moe stages over passes T=%d H=%d" % (T, H), flush=True)
+    g = np.random.default_rng([14, 8])
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = synth.uniform_f32(g, (T, k), 0.05, 0.3)
+    ex = synth.expert_set(18, 4, E, H, I, 64, experts=np.unique(ids), threads=16)
+    d = upload_experts(ex, only=np.unique(ids))
+    x = synth.activations(np.random.default_rng(19), (T, H), "bf16")
+    e = q.experts(4, 64, d["gate_q"], d["up_q"], d["down_q"], d["gate_s"], d["up_s"], d["down_s"])
+    ws = torch.empty(q.moe_expert_ffn_workspace(e, T, k), dtype=torch.uint8, device="cuda")
+    y1 = torch.full((T, H), float("nan"), device="cuda")
+    y2 = torch.full((T, H), float("nan"), device="cuda")
+    h = torch.empty((T * k, I), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(w)
+    q.moe_expert_ffn(e, xd, idd, wd, y1, ws)
+    q.moe_gate_up(e, xd, idd, h, ws)
+    q.moe_down(e, h, idd, wd, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    oracle.set_threads(16)
+    yr, _, nr = oracle.moe_ffn(ex, x, ids, w)
+    assert norm_err(host(y1), yr, nr) <= TOL
+
+
 @pytest.mark.parametrize("H,k,bad", [(2048, 8, False), (2048, 8, True), (2048, 4, False), (4096, 8, True)])
 def test_moe_small_experts(q, oracle, H, k, bad):
     """inter 512, one token (the small-expert decode layer), with fewer slots,
