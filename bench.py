@@ -44,7 +44,8 @@ def parse():
                         "the value is the number of rotating copies of it (one per layer of a model)")
     p.add_argument("--batch", type=int, default=1, help="gemv: activations per weight read (qgemm_small when > 1)")
     p.add_argument("--gs", type=int, default=64, help="int4 group size (0 = per-row)")
-    p.add_argument("--fmt", type=int, default=4, help="gemv: 4 = int4, 1 = int8 per-row, 5 = int3-g64 two-plane")
+    p.add_argument("--fmt", type=int, default=4, help="4 = int4, 1 = int8 per-row, 5 = int3-g64 two-plane "
+                                                      "(gemv and the moe decode configs)")
     p.add_argument("--n", type=int, default=6144)
     p.add_argument("--pair", type=int, default=0,
                    help="gemv: rows of a second matrix of the same x and format, run with qgemv_pair "
@@ -72,11 +73,16 @@ def dev(a):
 
 def expert_bytes(fmt, H, I, gs):
     """Weights + scales of one expert (gate, up, down), as stored."""
+    return 2 * I * row_bytes(fmt, H, gs) + H * row_bytes(fmt, I, gs)
+
+
+def row_bytes(fmt, k, gs):
+    """Weights + scales of one row of k inputs, as stored."""
     if fmt == 4:
-        gh = 1 if not gs else H // gs
-        gi = 1 if not gs else I // gs
-        return 2 * I * (H // 2 + 4 * gh) + H * (I // 2 + 4 * gi)
-    return 2 * I * (H + 4) + H * (I + 4)
+        return k // 2 + 4 * (k // gs if gs else 1)
+    if fmt == 5:  # int3-g64: 24 bytes + one scale per 64 inputs
+        return (k + 63) // 64 * 28
+    return k + 4
 
 
 def counter_traffic(name):
@@ -225,10 +231,12 @@ def bench_moe(args, E, H, I):
     from int4_expert_gemv_amd import qmoe, synth
     from oracle import ref
 
-    T, k, gs, fmt = args.tokens, 8, args.gs, 4
+    T, k, fmt = args.tokens, 8, args.fmt
+    gs = {1: 0, 5: 64}.get(fmt, args.gs)
+    wname = {1: "int8-row", 5: "int3-g64"}.get(fmt, "int4-" + ("g%d" % gs if gs else "row"))
     nsh = max(0, args.shared)
     n_steps = args.warmup + args.steps
-    print("generating %d experts (hidden %d, inter %d, int4 gs=%d)" % (E + nsh, H, I, gs), file=sys.stderr, flush=True)
+    print("generating %d experts (hidden %d, inter %d, %s)" % (E + nsh, H, I, wname), file=sys.stderr, flush=True)
     t0 = time.time()
     ex = synth.expert_set(args.seed, fmt, E + nsh, H, I, gs, threads=min(16, os.cpu_count() or 4), scales=args.scales)
     d = {key: dev(ex[key]) for key in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}
@@ -311,7 +319,7 @@ def bench_moe(args, E, H, I):
     ebytes = expert_bytes(fmt, H, I, gs)
     uniq = [len(np.unique(ids_h[args.warmup + j])) for j in range(args.steps)]
     step_bytes = float(np.mean(uniq)) * ebytes + T * H * 2 + T * H * 4 + T * k * 8
-    gu_bytes = float(np.mean(uniq)) * (2 * I * (H // 2 + 4 * (H // gs if gs else 1))) + T * H * 2
+    gu_bytes = float(np.mean(uniq)) * (2 * I * row_bytes(fmt, H, gs)) + T * H * 2
     value = step_bytes / (ms_step * 1e-3) / 1e9
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
 
@@ -322,8 +330,11 @@ def bench_moe(args, E, H, I):
                            1, step_bytes, args.cpu_seconds / 2, "the same decode steps (routing draws 0, 1, ...), "
                                                                  "fp64 oracle")
 
-    gname = "g%d" % gs if gs else "row"
+    gname = {1: "int8", 5: "int3"}.get(fmt, "g%d" % gs if gs else "row")
     tag = "%s_%s_t%d%s" % (args.config, gname, T, "_shared" if nsh else "")
+    arith = ("bf16 dot products (v_dot2: weight codes as exact bf16, x as bf16 hi + lo where it is fp32), "
+             "fp32 accumulation" if fmt == 5 else
+             "integer dot products (int4 x int4 digits, int8 matrix instructions) into int32, combined in fp32")
     routing = "top-%d" % k
     if nsh:
         routing = ("top-%d + 1 shared expert folded in as an always-on slot with weight 1 (%d rotating copies)"
@@ -334,13 +345,12 @@ def bench_moe(args, E, H, I):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i32+f32",
         "data": "synthetic (seeded; weight scales '%s')" % args.scales,
         "config": {"workload": "moe_expert_ffn decode: hidden %d, %d experts, inter %d, %s, %d token(s)%s, "
-                               "int4-%s weights, bf16 x" % (H, E, I, routing, T,
-                                                            " routed independently" if T > 1 else "", gname),
-                   "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": "int4-" + gname,
+                               "%s weights, bf16 x" % (H, E, I, routing, T,
+                                                      " routed independently" if T > 1 else "", wname),
+                   "tokens": T, "hidden": H, "experts": E, "inter": I, "top_k": k, "weights": wname,
                    "unique_experts_per_step": round(float(np.mean(uniq)), 2),
                    "bytes_per_step": int(step_bytes), "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4),
-                   "arithmetic": "integer dot products (int4 x int4 digits, int8 matrix instructions) into int32, "
-                                 "combined in fp32"},
+                   "arithmetic": arith},
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("moe_gate_up_%s_counters" % tag),

@@ -51,7 +51,11 @@
  *    i / 16 and at bit i of the little-endian high word; element = value - 4.
  *    Rows are ceil(k/64) * 24 bytes (a ragged last group is padded).
  *    group_size must be 64.  qgemv, qgemv_pair and qgemm_small with batch 1
- *    take it (k <= 16384); the expert FFN does not (QM_ERR_UNSUPPORTED).
+ *    take it (k <= 16384).  The expert FFN takes it through its decode
+ *    kernels for any number of tokens (hidden, inter <= 16384 and multiples
+ *    of 32; top_k * ceil(inter / 64) <= 512); it has no prefill kernels
+ *    (QM_PATH_PREFILL gives QM_ERR_UNSUPPORTED) [V: int3 commit notes, int3
+ *    expert matmuls and fused gate_up].
  *  Value = element * its scale.
  *
  * Arithmetic.  The int4 and int8 kernels apply the weights with integer dot
@@ -200,7 +204,9 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  * arrays), hidden % 512 == 0, inter % 256 == 0, n_experts <= 8192 -- and
  * otherwise the decode kernels pass by pass.  The decode kernels take
  * hidden up to 16384 (int4; 8192 int8) and inter up to 4096 (int4; 2048
- * int8); other shapes return QM_ERR_UNSUPPORTED.                           */
+ * int8); other shapes return QM_ERR_UNSUPPORTED.  int3-g64 experts run
+ * their own decode kernels for any n_tokens (each token's routed pairs read
+ * their expert rows; no union of experts across tokens).                  */
 QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
                    const int32_t *topk_ids, const float *topk_w, int32_t top_k,
                    float *y, void *workspace, size_t workspace_bytes, void *stream);

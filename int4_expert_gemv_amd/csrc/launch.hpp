@@ -76,6 +76,17 @@ int moe_decode_tokens_per_pass(int fmt, int topk, const ExpertArgs& e);
 hipError_t launch_moe_gate_up2(int fmt, int xdt, bool grouped, const MoeDecArgs& a, hipStream_t st);
 hipError_t launch_moe_down2(int fmt, bool grouped, const MoeDecArgs& a, bool h_from_caller, hipStream_t st);
 
+// moe_int3.hip: the expert FFN for int3-g64 experts (decode kernels, any
+// number of tokens).  Shapes they take; fp32 h bytes the fused call keeps in
+// the workspace; gate+up (h = silu(G x) * (U x), fp32 [T * topk][I]) and
+// down + weighted combine (y [T][H] from that h).
+bool moe_i3_supported(int topk, const ExpertArgs& e);
+size_t moe_i3_ws_bytes(int T, int topk, const ExpertArgs& e);
+hipError_t launch_moe_i3_gate_up(int xdt, const ExpertArgs& e, const void* x, const int32_t* ids, int T, int topk,
+                                 float* h, hipStream_t st);
+hipError_t launch_moe_i3_down(const ExpertArgs& e, const float* h, const int32_t* ids, const float* w, int T,
+                              int topk, float* y, hipStream_t st);
+
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
 // (or row length, per-row scales) is a multiple of 64 with at most 96 groups
 // per row (grouped: a multiple of 4 groups, 16-byte aligned scale arrays),

@@ -132,7 +132,6 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
 // Shapes, format and group size only (no pointers).
 bool moe_shape_ok(const qm_experts* ex) {
   if (ex->n_experts < 1 || ex->hidden < 1 || ex->inter < 1) return false;
-  if (ex->fmt == QM_FMT_INT3) return false;  // the expert kernels take int4 and int8
   if (check_shape(ex->fmt, ex->inter, ex->hidden, ex->group_size) != QM_OK) return false;
   if (check_shape(ex->fmt, ex->hidden, ex->inter, ex->group_size) != QM_OK) return false;
   const int gh = eff_gs(ex->fmt, ex->group_size, ex->hidden);
@@ -149,7 +148,6 @@ int check_experts(const qm_experts* ex) {
   if (a != QM_OK) return a;
   if (b != QM_OK) return b;
   if (ex->hidden < 1 || ex->inter < 1) return QM_ERR_UNSUPPORTED;
-  if (ex->fmt == QM_FMT_INT3) return QM_ERR_UNSUPPORTED;
   const void* q[3] = {ex->gate_q, ex->up_q, ex->down_q};
   const void* s[3] = {ex->gate_s, ex->up_s, ex->down_s};
   for (int i = 0; i < 3; ++i)
@@ -300,7 +298,11 @@ size_t moe_expert_ffn_workspace(const qm_experts* ex, int32_t n_tokens, int32_t 
   if (!ex || n_tokens < 0 || top_k < 1 || top_k > QM_TOPK_MAX) return 0;
   if (ex->hidden < 1 || ex->inter < 1 || ex->n_experts < 1) return 0;
   size_t need = 0;
-  if (moe_shape_ok(ex)) {
+  if (ex->fmt == QM_FMT_INT3) {
+    // int3: the fp32 hidden vectors between the two launches
+    if (moe_shape_ok(ex) && moe_i3_supported(top_k, expert_args(ex)))
+      need = moe_i3_ws_bytes(n_tokens, top_k, expert_args(ex));
+  } else if (moe_shape_ok(ex)) {
     const int tpp = dec_tokens(ex, top_k);
     if (tpp > 0) {
       const int td = n_tokens < tpp ? n_tokens : tpp;
@@ -327,6 +329,18 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
+  if (ex->fmt == QM_FMT_INT3) {  // decode kernels only, any number of tokens
+    const ExpertArgs e = expert_args(ex);
+    if (path == QM_PATH_PREFILL || !moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+      return QM_ERR_WORKSPACE;
+    float* h = static_cast<float*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = launch_moe_i3_gate_up(x_dtype, e, x, topk_ids, n_tokens, top_k, h, s);
+    if (err == hipSuccess) err = launch_moe_i3_down(e, h, topk_ids, topk_w, n_tokens, top_k, y, s);
+    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
@@ -369,6 +383,16 @@ int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(h, 4) || !aligned(topk_ids, 4)) return QM_ERR_UNSUPPORTED;
+  if (ex->fmt == QM_FMT_INT3) {
+    const ExpertArgs e = expert_args(ex);
+    if (!moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+      return QM_ERR_WORKSPACE;
+    const hipError_t err =
+        launch_moe_i3_gate_up(x_dtype, e, x, topk_ids, n_tokens, top_k, h, static_cast<hipStream_t>(stream));
+    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
@@ -398,6 +422,16 @@ int moe_down(const qm_experts* ex, const float* h, int32_t n_tokens, const int32
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(h, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
+  if (ex->fmt == QM_FMT_INT3) {
+    const ExpertArgs e = expert_args(ex);
+    if (!moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
+      return QM_ERR_WORKSPACE;
+    const hipError_t err =
+        launch_moe_i3_down(e, h, topk_ids, topk_w, n_tokens, top_k, y, static_cast<hipStream_t>(stream));
+    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
+  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;

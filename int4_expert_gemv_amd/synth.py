@@ -137,14 +137,19 @@ def expert_set(seed, fmt, n_experts, hidden, inter, gs, experts=None, threads=1,
     both take).  `experts` limits generation to a subset of ids; the other
     experts' slots are left zero (only valid when routing avoids them).
     `scales`: the scale draw range, see scale_range."""
-    G_h = n_groups(hidden, gs) if fmt == FMT_INT4 else 1
-    G_i = n_groups(inter, gs) if fmt == FMT_INT4 else 1
-    rb_h = hidden // 2 if fmt == FMT_INT4 else hidden
-    rb_i = inter // 2 if fmt == FMT_INT4 else inter
-    qdt = np.uint8 if fmt == FMT_INT4 else np.int8
+    if fmt == FMT_INT3:  # 24 bytes and one scale per 64 inputs (gs is 64)
+        gs = 64
+        G_h, G_i = (hidden + 63) // 64, (inter + 63) // 64
+        rb_h, rb_i = G_h * 24, G_i * 24
+    else:
+        G_h = n_groups(hidden, gs) if fmt == FMT_INT4 else 1
+        G_i = n_groups(inter, gs) if fmt == FMT_INT4 else 1
+        rb_h = hidden // 2 if fmt == FMT_INT4 else hidden
+        rb_i = inter // 2 if fmt == FMT_INT4 else inter
+    qdt = np.int8 if fmt == FMT_INT8_ROW else np.uint8
     out = {
         "n_experts": n_experts, "hidden": hidden, "inter": inter, "fmt": fmt,
-        "gs": int(gs or 0) if fmt == FMT_INT4 else 0,
+        "gs": int(gs or 0) if fmt in (FMT_INT4, FMT_INT3) else 0,
         "gate_q": np.zeros((n_experts, inter, rb_h), qdt),
         "up_q": np.zeros((n_experts, inter, rb_h), qdt),
         "down_q": np.zeros((n_experts, hidden, rb_i), qdt),

@@ -7,7 +7,8 @@ Format (colibri page "Vulkan backend: expert tier + dense + MLA attention on
 any Vulkan 1.2 GPU", commit notes on qmatmul.comp and "fmt=4 grouped
 scales"): int4 value = nibble - 8, two per byte with the low nibble first,
 one fp32 scale per gs consecutive inputs of a row (gs 0 = one per row);
-int8 per-row = two's complement with one fp32 scale per row.
+int8 per-row = two's complement with one fp32 scale per row; int3-g64 as
+in dense_int3.
 """
 import numpy as np
 
@@ -41,10 +42,31 @@ def dense_int8(q, scales, k):
     return vals, np.repeat(s, k, axis=1)
 
 
+def dense_int3(q, scales, k):
+    """int3-g64 (int3 commit notes of the same page): per 64-group 24 bytes,
+    four little-endian 32-bit words of 2-bit low parts (value i at bits
+    2 (i % 16) of word i // 16), then a little-endian 64-bit word of high
+    bits (value i at bit i); element = value - 4; one scale per group."""
+    q = np.asarray(q, dtype=np.uint8)
+    n = q.shape[0]
+    G = (k + 63) // 64
+    b = q.reshape(n, G, 24)
+    words = np.ascontiguousarray(b[:, :, :16]).view("<u4").astype(np.uint64)   # [n][G][4]
+    high = np.ascontiguousarray(b[:, :, 16:]).view("<u8")[:, :, 0]             # [n][G]
+    i = np.arange(64, dtype=np.uint64)
+    low = (words[:, :, i // 16] >> (2 * (i % 16))) & 3
+    hb = (high[:, :, None] >> i) & 1
+    vals = (low | (hb << 2)).astype(np.int64).reshape(n, G * 64)[:, :k] - 4
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64).reshape(n, G)
+    return vals.astype(np.float64), s[:, np.arange(k) // 64]
+
+
 def dense(fmt, q, scales, k, gs):
     """(values, per-element scales) as float64 [n][k]."""
     if fmt == 4:
         return dense_int4(q, scales, k, gs)
+    if fmt == 5:
+        return dense_int3(q, scales, k)
     return dense_int8(q, scales, k)
 
 

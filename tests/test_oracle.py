@@ -273,8 +273,60 @@ def pin_int3(o):
     assert np.array_equal(y3, y4) and np.array_equal(n3, n4)
 
 
+def _int3_layer(g, E, H, I):
+    """An int3-g64 layer from known values v in 0..7 and the int4-g64 layer
+    with nibbles v + 4 (the same elements v - 4) and the same scales."""
+    ex3 = {"n_experts": E, "hidden": H, "inter": I, "fmt": 5, "gs": 64}
+    ex4 = {"n_experts": E, "hidden": H, "inter": I, "fmt": 4, "gs": 64}
+    vals = {}
+    for name, n, k in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        v = g.integers(0, 8, (E, n, k))
+        s = g.uniform(0.5, 2.0, (E, n, k // 64)).astype(np.float32)
+        ex3[name + "_q"] = np.stack([pack_int3(v[e]) for e in range(E)])
+        ex4[name + "_q"] = np.stack([bf.pack_nibbles(v[e] + 4) for e in range(E)])
+        ex3[name + "_s"] = ex4[name + "_s"] = s
+        vals[name] = v
+    return ex3, ex4, vals
+
+
+def pin_int3_moe(o):
+    """A whole int3 layer: bit for bit the int4-g64 layer with nibbles v + 4
+    (y, h and the normaliser); the dense numpy restatement; and, with each
+    token's x one-hot on a column c, h = silu(a) * b with a, b the known
+    elements (v - 4) times their scales in column c, then y = sum_j w_j D h."""
+    E, H, I, T, k = 4, 192, 128, 3, 2
+    g = np.random.default_rng(15)
+    ex3, ex4, vals = _int3_layer(g, E, H, I)
+    x = g.standard_normal((T, H)).astype(np.float32)
+    ids = np.array([[0, 3], [2, 1], [3, 3]], np.int32)
+    w = np.array([[0.7, -1.3], [0.25, 2.0], [1.5, 0.5]], np.float32)
+    y3, h3, n3 = o.moe_ffn(ex3, x, ids, w, want_h=True)
+    y4, h4, n4 = o.moe_ffn(ex4, x, ids, w, want_h=True)
+    assert np.array_equal(y3, y4) and np.array_equal(h3, h4) and np.array_equal(n3, n4)
+    yb, nb = bf.moe(ex3, x, ids, w)
+    assert np.all(np.abs(y3 - yb) <= 1e-12 * nb) and np.all(np.abs(n3 - nb) <= 1e-12 * nb)
+    cols = [5, 64 + 17, 191]
+    xo = np.zeros((T, H), np.float32)
+    for t, c in enumerate(cols):
+        xo[t, c] = 1.0
+    yo, ho, _ = o.moe_ffn(ex3, xo, ids, w, want_h=True)
+    for t, c in enumerate(cols):
+        yt, nt = np.zeros(H), np.zeros(H)
+        for j in range(k):
+            e = ids[t, j]
+            a = (vals["gate"][e][:, c] - 4) * ex3["gate_s"][e][:, c // 64].astype(np.float64)
+            b = (vals["up"][e][:, c] - 4) * ex3["up_s"][e][:, c // 64].astype(np.float64)
+            h = a / (1.0 + np.exp(-a)) * b
+            assert _rel_close(ho[t * k + j], h, 1e-14)
+            D = (vals["down"][e] - 4) * np.repeat(ex3["down_s"][e].astype(np.float64), 64, axis=1)
+            yt += float(w[t, j]) * (D @ h)
+            nt += abs(float(w[t, j])) * (np.abs(D) @ np.abs(h))
+        assert np.all(np.abs(yo[t] - yt) <= 1e-12 * nt)
+
+
 def run_battery(o):
     pin_int3(o)
+    pin_int3_moe(o)
     pin_rmsnorm(o)
     pin_f64_input(o)
     pin_hand_gemv(o)
@@ -301,6 +353,10 @@ def test_hand_gemv(oracle):
 
 def test_int3_decode(oracle):
     pin_int3(oracle)
+
+
+def test_int3_moe_layer(oracle):
+    pin_int3_moe(oracle)
 
 
 def test_rmsnorm_closed_forms(oracle):
@@ -352,7 +408,7 @@ def test_every_nibble_in_every_position(oracle):
     assert np.all(np.abs(y - yb) <= 1e-13 * nb)
 
 
-@pytest.mark.parametrize("fmt,gs", [(4, 64), (4, 0), (1, 0)])
+@pytest.mark.parametrize("fmt,gs", [(4, 64), (4, 0), (1, 0), (5, 64)])
 def test_bruteforce_moe(oracle, fmt, gs):
     pin_bruteforce_moe(oracle, fmt, gs)
 
