@@ -200,7 +200,7 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  * larger batches run the expert-grouped prefill kernels (bf16 MFMA, hidden
  * vector and fp32 activations rounded to bf16) when the experts qualify --
  * int4 with a group size (or, per row, a row length) that is a multiple of
- * 64, at most 96 groups per row (a multiple of 4, with 16-byte aligned scale
+ * 64 (grouped: a multiple of 4 groups per row, with 16-byte aligned scale
  * arrays), hidden % 512 == 0, inter % 256 == 0, n_experts <= 8192 -- and
  * otherwise the decode kernels pass by pass.  The decode kernels take
  * hidden up to 16384 (int4; 8192 int8) and inter up to 4096 (int4; 2048

@@ -88,9 +88,9 @@ hipError_t launch_moe_i3_down(const ExpertArgs& e, const float* h, const int32_t
                               int topk, float* y, hipStream_t st);
 
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
-// (or row length, per-row scales) is a multiple of 64 with at most 96 groups
-// per row (grouped: a multiple of 4 groups, 16-byte aligned scale arrays),
-// hidden % 512 == 0, inter % 256 == 0 and at most 8192 experts.
+// (or row length, per-row scales) is a multiple of 64 (grouped: a multiple of
+// 4 groups per row, 16-byte aligned scale arrays), hidden % 512 == 0,
+// inter % 256 == 0 and at most 8192 experts.
 bool moe_prefill_supported(int fmt, int topk, const ExpertArgs& e);
 size_t moe_prefill_workspace(int T, int topk, const ExpertArgs& e);
 hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void* x, const int32_t* ids,

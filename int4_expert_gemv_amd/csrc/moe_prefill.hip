@@ -51,14 +51,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define QM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kBM = 32;         // tokens per M-tile (one 32-row MFMA subtile)
-constexpr int kBK = 128;        // K per pipeline stage (two 64-K chunks)
+constexpr int kBK = 256;        // K per pipeline stage: a 128-byte line of every weight row
 #ifndef QM_PF_STAGES
 #define QM_PF_STAGES 3
 #endif
 constexpr int kGW = 16;         // waves per GEMM workgroup
 constexpr int kGT = 64 * kGW;   // threads per GEMM workgroup
 constexpr int kStages = QM_PF_STAGES;  // LDS ring depth
-constexpr int kGMax = 96;       // scale groups per row the LDS correction table holds
 constexpr int kEMax = 8192;     // experts the bucketing block handles in LDS
 
 struct Tile {
@@ -231,21 +230,6 @@ __device__ __forceinline__ int rotated(int it, int rot, int n) {
   return v < n ? v : v - n;
 }
 
-// wait until at most n * U VMEM operations are outstanding (0 <= n <= D - 2)
-template <int U, int D>
-__device__ __forceinline__ void wait_stages(int n) {
-  static_assert(D >= 2 && D <= 5 && (D - 2) * U < 64, "ring depth");
-  if (n <= 0) {
-    wait_vm<0>();
-  } else if (n == 1 || D <= 3) {
-    wait_vm<(D >= 3 ? U : 0)>();
-  } else if (n == 2 || D <= 4) {
-    wait_vm<(D >= 4 ? 2 * U : 0)>();
-  } else {
-    wait_vm<(D >= 5 ? 3 * U : 0)>();
-  }
-}
-
 // The B operand is built in plain C so that the compiler sees every VALU
 // write feeding the MFMA and inserts the required wait states (an inline-asm
 // producer is opaque to its hazard tracking).  `base` is the bf16 pair
@@ -258,42 +242,50 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t base) {
   return __builtin_bit_cast(bf16x8, p);
 }
 
-// Block: 16 waves over one M-tile of BM = 32 rows (tokens) and 512 weight
-// rows; wave w owns the 32-column tile of weight rows [32 w, 32 w + 32): for
-// gate+up (NM = 2) waves 0-7 hold gate columns and waves 8-15 the up columns
-// of the same 256 outputs, for down (NM = 1) the 512 outputs.  Four waves per
-// SIMD keep the matrix cores, the VALU work that builds B operands and folds
-// groups, and the LDS reads of different waves overlapping.  Per stage
-// (128 K) the block DMAs into LDS:
-//   A  BM rows x 256 B, piece p of row r at slot p ^ (r & 15)  (waves 0-7, one piece each)
-//   B  512 weight rows x 64 B, piece p of row rr at slot p ^ ((rr >> 2) & 3)   (two per thread)
+// Block: 16 waves over one M-tile of BM = 32 rows (tokens) and 256 weight
+// rows.  Waves w and w + 8 own the same 32-column tile of weight rows
+// [32 (w & 7), 32 (w & 7) + 32) and split every stage's 256 K: wave w the
+// first 128 (chunks 0, 1), wave w + 8 the second (chunks 2, 3); their two
+// partial tiles are added in the epilogue.  For gate+up (NM = 2) tiles 0-3
+// are gate columns and tiles 4-7 the up columns of the same 128 outputs, for
+// down (NM = 1) the 256 outputs.  Four waves per SIMD keep the matrix cores,
+// the VALU work that builds B operands and folds groups, and the LDS reads
+// of different waves overlapping.
+//
+// A stage reads a whole 128-byte line of every weight row (K = 256), so each
+// line is fetched into L2 once: with half a line per stage the other half
+// was needed a stage later, by when the line had often been evicted by the
+// other workgroups' streams and came from HBM a second time.  Per stage the
+// block DMAs into one LDS ring slot:
+//   A   BM rows x 512 B, piece p of row r at slot p ^ (r & 15)
+//   B   256 weight rows x 128 B, piece p of row rr at slot p ^ ((rr >> 1) & 7)
+//   SC  (grouped scales) per weight row the aligned 16 bytes holding the
+//       scales of the stage's groups
+//   CR  (grouped scales) per A row the aligned 16 bytes holding the sums of
+//       the stage's groups, for the offset correction
 // so that the ds_read_b128 operand reads of 16 consecutive lanes hit distinct
-// banks.  Grouped scales move per window of four groups (2 gs_ch stages): one
-// aligned 16-byte piece per weight row (waves 8-15), DMA'd with the window's
-// first stage into one of two window slots outside the stage ring.  Every
-// scale piece is its own 64-byte line access, so loading each piece once per
-// window rather than once per stage halves that request stream, which costs
-// far more per byte than the weight rows.  With one scale per row (ROWSC) a
-// lane keeps its column's scale in a register and no scales move.  Waves 0-7
-// issue UA DMA operations per stage, waves 8-15 PB plus one on window starts:
-// that is what their vmcnt waits count; two stages stay in flight while one
-// is used.
+// banks.  Every wave issues four DMA operations per stage -- one A piece, two
+// B pieces, and one of the 288 SC/CR pieces (18 lanes each) -- which is what
+// its vmcnt waits count; two stages stay in flight while one is used.  With
+// one scale per row (ROWSC) a lane keeps its column's scale in a register, no
+// scales move and the correction sums are a 32-entry table.
 template <int NM, bool ROWSC_>
 struct GemmShape {
   static constexpr bool ROWSC = ROWSC_;
   static constexpr int BM = kBM;
-  static constexpr int ROWS = kGW * 32;
+  static constexpr int ROWS = kGW / 2 * 32;  // weight rows of a block
   static constexpr int BN = ROWS / NM;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * kBK * 2;
-  static constexpr int SLOT = B_OFF + ROWS * kBK / 2;                  // one ring stage
-  static constexpr int SW = ROWS * 16;                                 // one scale-window slot
-  static constexpr int SW_OFF = kStages * SLOT;                        // two window slots
-  static constexpr int CORR_OFF = SW_OFF + (ROWSC ? 0 : 2 * SW);       // correction table
-  static constexpr int PB = ROWS * 4 / kGT;         // B pieces per thread
-  static constexpr int UA = PB + 1;                 // DMA operations per stage, waves 0-7
-  static constexpr int CS = BM;                     // correction table row stride (floats)
-  static_assert(BM * 16 == kGT / 2 && ROWS == kGT / 2 && (ROWS * 4) % kGT == 0, "piece split");
+  static constexpr int SC_OFF = B_OFF + ROWS * kBK / 2;
+  static constexpr int CR_OFF = SC_OFF + ROWS * 16;
+  static constexpr int SLOT = ROWSC ? SC_OFF : CR_OFF + BM * 16;  // one ring stage
+  static constexpr int CORR_OFF = kStages * SLOT;                  // ROWSC: the 32 correction values
+  static constexpr int LDS = CORR_OFF + (ROWSC ? BM * 4 : 0);
+  static constexpr int XCH = kGW / 2 * 16 * 64 * 4;               // epilogue exchange (reuses the ring)
+  static constexpr int XP = ROWSC ? 0 : (ROWS + BM + kGW - 1) / kGW;  // SC/CR pieces per wave
+  static_assert(BM * 32 == kGT && ROWS * 8 == 2 * kGT, "piece split");
+  static_assert(LDS + 2 * BM * 4 <= 160 * 1024 && XCH <= LDS, "LDS budget");
 };
 
 template <int NM, typename T>
@@ -301,35 +293,39 @@ __device__ __forceinline__ T pick(T const (&v)[NM], int m) {
   return NM == 1 || m == 0 ? v[0] : v[NM - 1];
 }
 
-// DMA of one pipeline stage (A rows, weight rows) into LDS slot `slot`, plus
-// the scale window it starts (`win`) into window slot `wslot`.  `wave` and
-// `win` are wave-uniform (SGPRs), so the choices are scalar branches and each
-// wave issues exactly the operations its vmcnt waits count.
+// The four DMA operations of a wave for one pipeline stage into LDS slot
+// `slot`.  Every source address is fixed per thread except for the stage's
+// K offset (A: 512 bytes, B: 128 bytes, SC/CR: one 16-byte piece).
+struct StageSrc {
+  const uint16_t* arow;    // this thread's A row, its piece offset in elements
+  int apc;
+  const uint8_t* brow[2];  // its two B rows, piece offsets in bytes
+  int bpc[2];
+  const float* xrow;       // its SC or CR row (grouped scales), null for none
+};
+
 template <typename S>
-__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, bool win, int wslot, int wave, int gs_sh,
-                                            const uint16_t* arow, int apiece, const uint8_t* const* brow,
-                                            const int* bpiece, const float* srow) {
+__device__ __forceinline__ void issue_stage(char* lds, int st, int slot, int wave, int lane, int gs_sh,
+                                            const StageSrc& src) {
   char* sd = lds + slot * S::SLOT;
-  const int k0 = st * kBK;
-  if (wave < kGW / 2) {
-    __builtin_amdgcn_global_load_lds(arow + k0 + 8 * apiece, QM_LDS_PTR(sd + S::A_OFF + wave * 1024), 16, 0, 0);
-  } else if constexpr (!S::ROWSC) {
-    if (win)  // the aligned four scales of the window
-      __builtin_amdgcn_global_load_lds(srow + (((st * 2) >> gs_sh) & ~3),
-                                       QM_LDS_PTR(lds + S::SW_OFF + wslot * S::SW + (wave - kGW / 2) * 1024), 16, 0,
-                                       0);
-  }
+  __builtin_amdgcn_global_load_lds(src.arow + st * kBK + src.apc, QM_LDS_PTR(sd + S::A_OFF + wave * 1024), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < S::PB; ++i)
-    __builtin_amdgcn_global_load_lds(brow[i] + k0 / 2 + 16 * bpiece[i],
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(src.brow[i] + st * (kBK / 2) + src.bpc[i],
                                      QM_LDS_PTR(sd + S::B_OFF + (i * kGW + wave) * 1024), 16, 0, 0);
+  if constexpr (!S::ROWSC) {
+    // the aligned four groups holding the stage's first group
+    const int piece = ((st * 4) >> gs_sh) >> 2;
+    if (lane < S::XP)
+      __builtin_amdgcn_global_load_lds(src.xrow + 4 * piece, QM_LDS_PTR(sd + S::SC_OFF + wave * S::XP * 16), 16, 0, 0);
+  }
 }
 
 // GM, the scale grouping the loop is compiled for: 0 one scale per row,
 // 1 groups of 64 K (every chunk starts and ends a group), 2 groups of 128 K
-// (chunk 0 of a stage starts one, chunk 1 ends it), 3 groups of 256 K or
-// more (decided at run time).  Where a chunk starts a group at compile time
-// its first MFMA takes the inline constant 0 as C.
+// or more (a wave's two chunks of a stage lie in one group).  Where a chunk
+// starts a group at compile time its first MFMA takes the inline constant 0
+// as C.
 template <int NM, int GM>
 __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   constexpr bool ROWSC = GM == 0;
@@ -354,123 +350,102 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
   }
   __syncthreads();
 
-  float* corr = reinterpret_cast<float*>(lds + S::CORR_OFF);
   const int nstages = a.K / kBK;
   const int h = lane >> 5, c32 = lane & 31;
-  const int mat = wave / (kGW / NM);  // this wave's matrix
-  const int rw = wave * 32 + c32;     // its weight row within the block
-  // correction table sources, loaded before the first DMA so that waiting
-  // for them leaves the stages in flight: corr[g][m] = -136 * (sum of group g of A row m)
-  constexpr int CT = (kBM * kGMax + kGT - 1) / kGT;
-  float cv[CT];
-#pragma unroll
-  for (int j = 0; j < CT; ++j) {
-    const int idx = tid + j * kGT;
-    cv[j] = idx < S::BM * a.G ? a.asum[(int64_t)s_row[idx / a.G] * a.G + idx % a.G] : 0.f;
-  }
-  // one scale per row: this lane's column
-  const float rsc = ROWSC ? pick(a.wsc, mat)[(int64_t)tl.e * a.es + n0 + (wave % (kGW / NM)) * 32 + c32] : 0.f;
+  const int kh = wave / HW, wl = wave % HW;  // K half of the stage, column tile
+  const int mat = wl / (HW / NM);            // this wave's matrix
+  const int rw = wl * 32 + c32;              // its weight row within the block
+  // one scale per row: this lane's column, and the correction values of the
+  // A rows (-136 * the row's sum)
+  const float rsc = ROWSC ? pick(a.wsc, mat)[(int64_t)tl.e * a.es + n0 + (wl % (HW / NM)) * 32 + c32] : 0.f;
+  float* corr0 = reinterpret_cast<float*>(lds + S::CORR_OFF);
+  if (ROWSC && tid < S::BM) corr0[tid] = -136.f * a.asum[s_row[tid]];
   // per-thread DMA sources (rows fixed for the whole K loop)
-  const uint16_t* arow = a.a;
-  int apiece = 0;
-  const float* srow = a.wsc[0];
-  if (wave < HW) {
-    const int P = wave * 64 + lane;
-    const int r = P >> 4;
-    arow = a.a + (int64_t)s_row[r] * a.K;
-    apiece = (P & 15) ^ (r & 15);
-  } else {
-    const int rr = (wave - HW) * 64 + lane;
-    srow = pick(a.wsc, rr / S::BN) + (int64_t)tl.e * a.es + (int64_t)(n0 + rr % S::BN) * a.G;
+  StageSrc src;
+  {
+    const int P = wave * 64 + lane;  // A piece: row P >> 5, slot P & 31
+    const int r = P >> 5;
+    src.arow = a.a + (int64_t)s_row[r] * a.K;
+    src.apc = 8 * ((P & 31) ^ (r & 15));
   }
-  const uint8_t* brow[S::PB];
-  int bpiece[S::PB];
 #pragma unroll
-  for (int i = 0; i < S::PB; ++i) {
-    const int P = (i * kGW + wave) * 64 + lane;
-    const int rr = P >> 2;
-    brow[i] = pick(a.wq, rr / S::BN) + (int64_t)tl.e * a.eq + (int64_t)(n0 + rr % S::BN) * a.rb;
-    bpiece[i] = (P & 3) ^ ((rr >> 2) & 3);
+  for (int i = 0; i < 2; ++i) {
+    const int P = (i * kGW + wave) * 64 + lane;  // B piece: row P >> 3, slot P & 7
+    const int rr = P >> 3;
+    src.brow[i] = pick(a.wq, rr / S::BN) + (int64_t)tl.e * a.eq + (int64_t)(n0 + rr % S::BN) * a.rb;
+    src.bpc[i] = 16 * ((P & 7) ^ ((rr >> 1) & 7));
   }
-  // Blocks walk K from different stages (rotated by whole scale groups):
-  // weight rows lie a multiple of 1 KiB apart, so blocks that all stood at the
-  // same K offset would all hit the same few L2 channels.  The rotation
-  // depends on the expert and the column tile only, never on which M-tile a
-  // pair landed in (the bucketing order is not fixed), so every output keeps
-  // one summation order from run to run.
-  // Rotation by whole scale windows keeps window starts at loop positions
-  // that are multiples of the window length, so loop position it uses
-  // window slot (it / window) & 1.
-  const int wsh = ROWSC ? 0 : a.gs_sh + 1;  // log2 of the stages per scale window
-  const int rk = tl.e * 7 + nti * 3;
-  const int rot = ROWSC ? rk % nstages : (rk % (nstages >> wsh)) << wsh;
+  src.xrow = nullptr;
+  if constexpr (!ROWSC) {
+    const int X = wave * S::XP + (lane < S::XP ? lane : 0);  // SC piece X < ROWS, then CR pieces
+    if (X < S::ROWS)
+      src.xrow = pick(a.wsc, X / S::BN) + (int64_t)tl.e * a.es + (int64_t)(n0 + X % S::BN) * a.G;
+    else
+      src.xrow = a.asum + (int64_t)s_row[min(X - S::ROWS, S::BM - 1)] * a.G;
+  }
+  // Blocks walk K from different stages: weight rows lie a multiple of
+  // 1 KiB apart, so blocks that all stood at the same K offset would all hit
+  // the same few L2 channels.  The rotation depends on the expert and the
+  // column tile only, never on which M-tile a pair landed in (the bucketing
+  // order is not fixed), so every output keeps one summation order from run
+  // to run.
+  const int rot = (tl.e * 7 + nti * 3) % nstages;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < nstages)
-      issue_stage<S>(lds, rotated(i, rot, nstages), i, (i & ((1 << wsh) - 1)) == 0, (i >> wsh) & 1, wave, a.gs_sh, arow,
-                     apiece, brow, bpiece, srow);
-#pragma unroll
-  for (int j = 0; j < CT; ++j) {
-    const int idx = tid + j * kGT;
-    if (idx < S::BM * a.G) corr[(idx % a.G) * S::CS + idx / a.G] = -136.f * cv[j];
-  }
+    if (i < nstages) issue_stage<S>(lds, rotated(i, rot, nstages), i, wave, lane, a.gs_sh, src);
 
   uint32_t base = 0x43004300u;
   asm volatile("" : "+v"(base));  // keep the constant in a VGPR (see b_operand)
   f32x16 acc = {}, tmp = {};
   for (int it = 0; it < nstages; ++it) {
-    // stages issued after this one so far: min(it + kStages - 2, nstages - 1) - it
+    // the wave's DMA operations of stage it + 1 (four; three without scales)
+    // may stay in flight
     static_assert(kStages == 3, "the waits below count one stage in flight");
-    const int ahead = min(kStages - 2, nstages - 1 - it);
-    if (wave < HW)
-      wait_stages<S::UA, kStages>(ahead);
-    else if (!ROWSC && ahead > 0 && ((it + 1) & ((1 << wsh) - 1)) == 0)
-      wait_stages<S::PB + 1, kStages>(ahead);  // the stage in flight carries a scale window
+    if (it + 1 < nstages)
+      wait_vm<ROWSC ? 3 : 4>();
     else
-      wait_stages<S::PB, kStages>(ahead);
+      wait_vm<0>();
     ring_barrier();  // this stage is in LDS for every wave; the previous one's slot is free
     const char* sd = lds + (it % kStages) * S::SLOT;
-    const char* sw = lds + S::SW_OFF + ((it >> wsh) & 1) * S::SW;  // this stage's scale window
     const int st = rotated(it, rot, nstages);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int chunk = st * 2 + c;
-      const int g = chunk >> a.gs_sh, cin = chunk & (a.gs_ch - 1);
-      // With one scale per row the group spans the whole (rotated) loop and
-      // the chain runs on from the zeroed tmp; with run-time groups the fold
-      // clears tmp for the next group.
+      const int chunk = st * 4 + 2 * kh + c;  // 64-K chunk of the row
+      const int g = chunk >> a.gs_sh;
+      // With one scale per row the chain runs on over the whole (rotated)
+      // loop from the zeroed tmp; with groups of 128 K or more a wave's two
+      // chunks of a stage lie in one group and are folded together.
       const bool first = GM == 1 ? true : GM == 2 ? c == 0 : false;
-      const bool last = GM == 1   ? true
-                        : GM == 2 ? c == 1
-                        : GM == 0 ? (it == nstages - 1 && c == 1)
-                                  : cin == a.gs_ch - 1;
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(sd + S::B_OFF + rw * 64 + 16 * ((2 * c + h) ^ ((rw >> 2) & 3)));
+      const bool last = GM == 1 ? true : GM == 2 ? c == 1 : (it == nstages - 1 && c == 1);
+      const u32x4 wv =
+          *reinterpret_cast<const u32x4*>(sd + S::B_OFF + rw * 128 + 16 * ((4 * kh + 2 * c + h) ^ ((rw >> 1) & 7)));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 bo = b_operand(wv[s], base);
-        const int p = 8 * c + 4 * h + s;
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const bf16x8 bo = b_operand(wv[s4], base);
+        const int p = 16 * kh + 8 * c + 4 * h + s4;
         const bf16x8 ao =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + c32 * 256 + 16 * (p ^ (c32 & 15))));
-        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo, (first && s == 0) ? f32x16{} : tmp, 0, 0, 0);
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sd + S::A_OFF + c32 * 512 + 16 * (p ^ (c32 & 15))));
+        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo, (first && s4 == 0) ? f32x16{} : tmp, 0, 0, 0);
       }
-      if (last) {  // last chunk of the group: fold with the column's scale
-        const float sc = ROWSC ? rsc : *reinterpret_cast<const float*>(sw + rw * 16 + (g & 3) * 4);
+      if (last) {  // last chunk of the group (or of the wave's part of it in this stage): fold with its scale
+        const float sc = ROWSC ? rsc : *reinterpret_cast<const float*>(sd + S::SC_OFF + rw * 16 + (g & 3) * 4);
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(sc, tmp[i], acc[i]);
-        if (GM == 3) tmp = f32x16{};
       }
     }
-    // Offset correction of the groups that ended in this stage, acc[m][n] +=
-    // sc[n][g] * corr[g][m], as one fp32 MFMA 32x32x2 whose two K slots are
-    // the stage's two chunks (lane half h holds chunk h: its group's
-    // correction if the group ends there, else 0, and that group's scale).
-    const int gfirst = (st * 2) >> a.gs_sh, glast = (st * 2 + 1) >> a.gs_sh;
-    const bool end0 = GM == 1 ? true : GM == 3 ? ((st * 2) & (a.gs_ch - 1)) == a.gs_ch - 1 : false;
-    const bool end1 = GM == 1 || GM == 2 ? true : GM == 0 ? it == nstages - 1 : ((st * 2 + 1) & (a.gs_ch - 1)) == a.gs_ch - 1;
-    if (end0 || end1) {
-      const int gh = h ? glast : gfirst;
-      const float av = (h ? end1 : end0) ? corr[gh * S::CS + c32] : 0.f;
-      const float bv = ROWSC ? rsc : *reinterpret_cast<const float*>(sw + rw * 16 + (gh & 3) * 4);
+    // Offset correction of the groups that end in this wave's chunks,
+    // acc[m][n] += sc[n][g] * (-136 * sum of group g of A row m), as one fp32
+    // MFMA 32x32x2 whose two K slots are the wave's two chunks (lane half h
+    // holds chunk h: its group's correction if the group ends there, else 0,
+    // and that group's scale).
+    const int ch = st * 4 + 2 * kh + h;
+    const int gh = ch >> a.gs_sh;
+    const bool endh = GM == 0 ? (it == nstages - 1 && kh == 1 && h == 1) : (ch & (a.gs_ch - 1)) == a.gs_ch - 1;
+    const bool any = GM == 0 ? (it == nstages - 1 && kh == 1) : GM == 1 ? true : ((st * 4 + 2 * kh + 1) & (a.gs_ch - 1)) == a.gs_ch - 1;
+    if (any) {
+      const float av =
+          !endh ? 0.f : ROWSC ? corr0[c32] : -136.f * *reinterpret_cast<const float*>(sd + S::CR_OFF + c32 * 16 + (gh & 3) * 4);
+      const float bv = ROWSC ? rsc : *reinterpret_cast<const float*>(sd + S::SC_OFF + rw * 16 + (gh & 3) * 4);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     // The next DMA goes out after this stage's compute: when the memory
@@ -479,28 +454,38 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
     // The slot it fills was released at this iteration's barrier.
     if (it + kStages - 1 < nstages) {
       const int j = it + kStages - 1;
-      issue_stage<S>(lds, rotated(j, rot, nstages), j % kStages, (j & ((1 << wsh) - 1)) == 0, (j >> wsh) & 1, wave,
-                     a.gs_sh, arow, apiece, brow, bpiece, srow);
+      issue_stage<S>(lds, rotated(j, rot, nstages), j % kStages, wave, lane, a.gs_sh, src);
     }
   }
 
   // epilogue; C layout: element 4i + j of a lane is row 8i + 4h + j, column lane & 31
-  if constexpr (NM == 2) {
-    // the up waves hand their tiles to the gate waves of the same columns
-    __syncthreads();  // every wave is done with the ring (no DMA outstanding after the last stage)
-    float* xch = reinterpret_cast<float*>(lds);
-    if (wave >= HW) {
+  __syncthreads();  // every wave is done with the ring (no DMA outstanding after the last stage)
+  float* xch = reinterpret_cast<float*>(lds);
+  // the second K halves join the first
+  if (kh == 1) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xch[((wave - HW) * 16 + i) * 64 + lane] = acc[i];
+    for (int i = 0; i < 16; ++i) xch[(wl * 16 + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += xch[(wl * 16 + i) * 64 + lane];
+  }
+  if constexpr (NM == 2) {
+    // the up tiles join the gate tiles of the same columns
+    __syncthreads();
+    if (kh == 0 && wl >= HW / 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xch[((wl - HW / 2) * 16 + i) * 64 + lane] = acc[i];
     }
     __syncthreads();
-    if (wave < HW) {
-      const int col = n0 + wave * 32 + c32;
+    if (kh == 0 && wl < HW / 2) {
+      const int col = n0 + wl * 32 + c32;
       const int pc = (col & ~7) | ((col & 7) < 4 ? 2 * (col & 7) : 2 * (col & 7) - 7);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + 4 * h + (i & 3);
-        const float up = xch[(wave * 16 + i) * 64 + lane];
+        const float up = xch[(wl * 16 + i) * 64 + lane];
         const uint32_t hb = f32_to_bf16_bits(silu(acc[i]) * up);
         const float sum = group_sum<32>(bf16_bits_to_f32(hb));
         if (row < tl.mrows) {
@@ -511,25 +496,26 @@ __global__ __launch_bounds__(kGT) void prefill_gemm_kernel(GemmArgs<NM> a) {
       }
     }
   } else {
-    const int col = n0 + wave * 32 + c32;
+    if (kh == 0) {
+      const int col = n0 + wl * 32 + c32;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * h + (i & 3);
-      if (row < tl.mrows) a.out[(int64_t)s_pair[row] * a.N + col] = acc[i];
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+        if (row < tl.mrows) a.out[(int64_t)s_pair[row] * a.N + col] = acc[i];
+      }
     }
   }
 }
 
 template <int NM>
-hipError_t launch_gemm(const GemmArgs<NM>& g, int blocks, size_t lds, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs<NM>& g, int blocks, hipStream_t st) {
+  constexpr size_t lds_row = GemmShape<NM, true>::LDS, lds_grp = GemmShape<NM, false>::LDS;
   if (g.G == 1)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 0>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 0>), dim3(blocks), dim3(kGT), lds_row, st, g);
   else if (g.gs_ch == 1)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 1>), dim3(blocks), dim3(kGT), lds, st, g);
-  else if (g.gs_ch == 2)
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 2>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 1>), dim3(blocks), dim3(kGT), lds_grp, st, g);
   else
-    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 3>), dim3(blocks), dim3(kGT), lds, st, g);
+    hipLaunchKernelGGL((prefill_gemm_kernel<NM, 2>), dim3(blocks), dim3(kGT), lds_grp, st, g);
   return hipGetLastError();
 }
 
@@ -606,10 +592,9 @@ Layout layout(int T, int topk, int E, int H, int I, int G_h, int G_i) {
 
 bool moe_prefill_supported(int fmt, int topk, const ExpertArgs& e) {
   if (fmt != kFmtInt4 || topk < 1 || topk > kTopkMax) return false;
-  if (e.E > kEMax || e.H % 512 || e.I % 256) return false;  // down N-tile 512, gate+up N-tile 256
+  if (e.E > kEMax || e.H % 512 || e.I % 256) return false;  // K in stages of 256; N-tiles 256 (down), 128 (gate+up)
   const int gsh = e.H / e.G_h, gsi = e.I / e.G_i;  // group sizes (== K when per row)
   if (gsh % 64 || gsi % 64) return false;
-  if (e.G_h > kGMax || e.G_i > kGMax) return false;
   // grouped scales move as aligned 16-byte pieces: G a multiple of 4, 16-byte aligned scale arrays
   auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   if (e.G_h > 1 && (e.G_h % 4 || !al16(e.gs) || !al16(e.us))) return false;
@@ -693,8 +678,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.h = hs;
     g.h32 = h32;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
-    const size_t lds = (size_t)Sh::CORR_OFF + (size_t)e.G_h * Sh::CS * 4;
-    err = launch_gemm<2>(g, blocks, lds, st);
+    err = launch_gemm<2>(g, blocks, st);
     if (err != hipSuccess) return err;
   }
 
@@ -736,8 +720,7 @@ hipError_t launch_moe_prefill(int fmt, int xdt, const ExpertArgs& e, const void*
     g.nt = e.H / Sh::BN;
     g.out = out;
     const int blocks = (Ly.mt_max * g.nt + 7) / 8 * 8;
-    const size_t lds = (size_t)Sh::CORR_OFF + (size_t)e.G_i * Sh::CS * 4;
-    err = launch_gemm<1>(g, blocks, lds, st);
+    err = launch_gemm<1>(g, blocks, st);
     if (err != hipSuccess) return err;
   }
 

@@ -75,6 +75,13 @@ def test_prefill_group_128(q, oracle):
     _case(q, oracle, 2, 4, 128, 8, 1024, 512, 24, 4)
 
 
+def test_prefill_group_256(q, oracle):
+    """Groups as long as a whole pipeline stage: each group's offset
+    correction is applied once, by the wave holding the stage's second K
+    half, while both halves fold their partial sums."""
+    _case(q, oracle, 11, 4, 256, 8, 1024, 1024, 40, 4)
+
+
 def test_prefill_fp32_activations(q, oracle):
     _case(q, oracle, 3, 4, 64, 16, 512, 256, 33, 4, xdt="f32")
 
