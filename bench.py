@@ -85,12 +85,15 @@ def row_bytes(fmt, k, gs):
     return k + 4
 
 
-def counter_traffic(name):
+def counter_traffic(name, sources=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary
     (profiles/<name>.txt: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled
     by the factor a plain 1 GiB copy gives), or None when the summary is
-    missing or was taken from other kernel sources than the ones built now."""
+    missing or was taken from other kernel sources than the ones built now
+    (`sources`: the source files its digest covers; the decode kernels'
+    by default)."""
     from int4_expert_gemv_amd import build as hipbuild
+    sources = hipbuild.DECODE_SOURCES if sources is None else sources
     path = os.path.join(ROOT, "profiles", name + ".txt")
     if not os.path.exists(path):
         return None
@@ -100,7 +103,7 @@ def counter_traffic(name):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("source_digest") != hipbuild.source_digest(hipbuild.DECODE_SOURCES) or \
+    if kv.get("source_digest") != hipbuild.source_digest(sources) or \
             "traffic_bytes_per_launch" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
@@ -373,7 +376,7 @@ def bench_prefill(args):
     uses one of 4 routing draws; every call streams the ~252 experts it
     touches (5.3 GB, far past the last-level cache)."""
     import torch
-    from int4_expert_gemv_amd import qmoe, synth
+    from int4_expert_gemv_amd import build as hipbuild, qmoe, synth
     from oracle import ref
 
     T, E, H, I, k, gs, fmt = 512, 256, 6144, 2048, 8, 64, 4
@@ -441,7 +444,8 @@ def bench_prefill(args):
                                    "top-8 Zipf routing, int4-g64 weights, bf16 MFMA",
                        "experts_touched": touched, "bytes_per_step": int(step_bytes), "gflop_per_step": flops / 1e9},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": counter_traffic("moe_prefill_512tok_g64_counters", hipbuild.PREFILL_SOURCES),
                          "kernel": "whole prefill layer (5 kernels)",
                          "mfma_tflops": round(tflops, 2), "mfma_peak_tflops": MFMA_PEAK,
                          "mfma_utilisation": round(tflops / MFMA_PEAK, 4)},

@@ -28,13 +28,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // LDS image of nq staged "units" (a unit is one 64-wide group of one
 // activation vector; unit q = v * G + g for vector v, group g):
-//   hi[(2 w + h) * nq + q]  u32x4: bf16 pairs (x_{16w+4h+c}, x_{16w+4h+c+8}),
+//   hi[kUnitV q + 2 w + h]  u32x4: bf16 pairs (x_{16w+4h+c}, x_{16w+4h+c+8}),
 //                           c = 0..3, of the unit's word w (16 values)
 //   lo[...]                 the same for x - hi (fp32 activations only)
 //   wsum[w * nq + q]        sum of word w's staged values
 //   corr[q]                 -132 * sum of the unit's staged values
-// Units are innermost, so lanes that take consecutive units read
-// consecutive 16-byte slots (no bank conflicts).
+// A unit's eight slots are padded to nine (144 bytes, 9 coprime with the 16
+// slots of a bank cycle), so 16 lanes that take consecutive units read 16
+// distinct bank groups, and a slot's offset within its unit is a constant.
+constexpr int kUnitV = 9;
 struct I3Lds {
   u32x4* hi;
   u32x4* lo;
@@ -44,14 +46,14 @@ struct I3Lds {
 };
 
 __host__ __device__ constexpr size_t i3_lds_bytes(int nq, bool split) {
-  return (size_t)nq * (128u * (split ? 2u : 1u) + 16u + 4u);
+  return (size_t)nq * (16u * kUnitV * (split ? 2u : 1u) + 16u + 4u);
 }
 
 __device__ __forceinline__ I3Lds i3_carve(void* base, int nq, bool split) {
   I3Lds L;
   L.hi = reinterpret_cast<u32x4*>(base);
-  L.lo = L.hi + 8 * nq;
-  L.wsum = reinterpret_cast<float*>(L.hi + (split ? 16 : 8) * nq);
+  L.lo = L.hi + kUnitV * nq;
+  L.wsum = reinterpret_cast<float*>(L.hi + (split ? 2 : 1) * kUnitV * nq);
   L.corr = L.wsum + 4 * nq;
   L.nq = nq;
   return L;
@@ -67,7 +69,7 @@ template <bool SPLIT, typename SrcF>
 __device__ __forceinline__ void i3_stage(const I3Lds& L, int G, int k, bool bf16x, SrcF src, int tid, int nthr) {
   const int nq = L.nq;
   for (int i = tid; i < 4 * nq; i += nthr) {
-    const int w = i / nq, q = i - w * nq;
+    const int q = i >> 2, w = i & 3;  // consecutive threads read consecutive words of x
     const int v = q / G, g = q - v * G;
     const int c0 = 64 * g + 16 * w;
     float val[16];
@@ -110,11 +112,11 @@ __device__ __forceinline__ void i3_stage(const I3Lds& L, int G, int k, bool bf16
         sum += bf16_bits_to_f32(la) + bf16_bits_to_f32(lb);
       }
     }
-    L.hi[(2 * w) * nq + q] = hp[0];
-    L.hi[(2 * w + 1) * nq + q] = hp[1];
+    L.hi[kUnitV * q + 2 * w] = hp[0];
+    L.hi[kUnitV * q + 2 * w + 1] = hp[1];
     if constexpr (SPLIT) {
-      L.lo[(2 * w) * nq + q] = lp[0];
-      L.lo[(2 * w + 1) * nq + q] = lp[1];
+      L.lo[kUnitV * q + 2 * w] = lp[0];
+      L.lo[kUnitV * q + 2 * w + 1] = lp[1];
     }
     L.wsum[w * nq + q] = sum;
   }
@@ -144,18 +146,19 @@ __device__ __forceinline__ I3Group i3_load(const uint8_t* p) {
 // one independent dot chain per low word
 template <bool SPLIT>
 __device__ __forceinline__ float i3_group_dot(const I3Group& wg, const I3Lds& L, int q) {
-  const int nq = L.nq;
+  const u32x4* xh = L.hi + kUnitV * q;
+  const u32x4* xl = L.lo + kUnitV * q;
   const uint32_t lo[4] = {wg.w[0][0], wg.w[0][1], wg.w[1][0], wg.w[1][1]};
   float part[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t h16 = (wg.w[2][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
     const uint32_t t = ((h16 & 0xFFu) | ((h16 & 0xFF00u) << 8)) << 2;
-    const u32x4 x0 = L.hi[(2 * j) * nq + q], x1 = L.hi[(2 * j + 1) * nq + q];
+    const u32x4 x0 = xh[2 * j], x1 = xh[2 * j + 1];
     u32x4 l0, l1;
     if constexpr (SPLIT) {
-      l0 = L.lo[(2 * j) * nq + q];
-      l1 = L.lo[(2 * j + 1) * nq + q];
+      l0 = xl[2 * j];
+      l1 = xl[2 * j + 1];
     }
     float c = j == 0 ? L.corr[q] : 0.f;
 #pragma unroll
