@@ -44,10 +44,12 @@ constexpr int kTopkMax = 32;  // largest top_k accepted by the C ABI
 
 constexpr int kFmtInt8 = 1;
 constexpr int kFmtInt4 = 4;
+constexpr int kFmtInt3 = 5;
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

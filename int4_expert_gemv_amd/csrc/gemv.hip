@@ -4,10 +4,14 @@
 // expert tier + dense + MLA attention on any Vulkan 1.2 GPU" (commit notes
 // "backend_vulkan.c/.h + shaders/qmatmul.comp", the S-token batch of the same
 // shader, and "fmt=4 grouped scales"), int4 (grouped or per row) and int8 per
-// row, on the activation digit planes of planes.hpp.
+// row, and int3-g64 (the int3 commit notes of the same page; as signed
+// nibbles, planes.hpp), on the activation digit planes of planes.hpp.
 //
 // Work split.  A persistent grid of about one workgroup (eight waves) per CU.
-// A row's inputs are cut into 16-byte chunks (32 int4 or 16 int8 weights);
+// A row's inputs are cut into chunks of 32 int4 (16 bytes), 16 int8 (16
+// bytes) or 32 int3 weights (12 bytes: half a 24-byte group -- two low-part
+// words and their 32 high bits -- turned into four signed-nibble words when
+// used);
 // lane l takes chunks l + 64 i of every row.  The reduction runs over
 // segments of 64 * CPL chunks (one segment covers a row when the digit planes
 // of all its activations fit the LDS budget).  Per segment the workgroup
@@ -35,8 +39,8 @@ constexpr int kGvItems = 1024;  // activation groups staged per segment (two per
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int FMT> constexpr int per_chunk() { return FMT == kFmtInt4 ? 32 : 16; }
-template <int FMT> constexpr int words_per_group() { return FMT == kFmtInt4 ? 16 : 8; }
+template <int FMT> constexpr int per_chunk() { return FMT == kFmtInt8 ? 16 : 32; }
+template <int FMT> constexpr int words_per_group() { return FMT == kFmtInt8 ? 8 : 16; }
 
 // LDS: two planes of digit words [2][NB][SEGC][W] plus factors [NB][SEGC] and
 // the plane-count slot.  (One group per chunk: 32 activations against int4,
@@ -93,7 +97,14 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
       for (int i = 0; i < CPL; ++i) {
         const int c = c0 + lane + 64 * i;
         if (c < kch) {
-          wv[u][i] = ld_stream(rr.q + (int64_t)c * 16);
+          if constexpr (FMT == kFmtInt3) {  // group c / 2: low words 2 (c & 1), +1 and their 32 high bits
+            const uint8_t* gp = rr.q + (int64_t)(c >> 1) * 24;
+            const u32x2 lw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(gp + 8 * (c & 1)));
+            const uint32_t hw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(gp + 16 + 4 * (c & 1)));
+            wv[u][i] = u32x4{lw[0], lw[1], hw, 0u};
+          } else {
+            wv[u][i] = ld_stream(rr.q + (int64_t)c * 16);
+          }
           if constexpr (GROUPED) sv[u][i] = ld_stream(rr.s + (c >> gshift));
         }
       }
@@ -118,6 +129,12 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
       for (int u = 0; u < NU; ++u) {
         w[u] = wv[u][i];
         if constexpr (FMT == kFmtInt4) w[u] ^= 0x88888888u;
+        if constexpr (FMT == kFmtInt3) {
+          uint32_t e0, o0, e1, o1;
+          i3_words(wv[u][i][0], wv[u][i][2] & 0xFFFFu, e0, o0);
+          i3_words(wv[u][i][1], wv[u][i][2] >> 16, e1, o1);
+          w[u] = u32x4{e0, o0, e1, o1};
+        }
       }
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
           }
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            const int S = FMT == kFmtInt4 ? gdot_i4(w[u], xw) : gdot_i8(w[u], xw);
+            const int S = FMT == kFmtInt8 ? gdot_i8(w[u], xw) : gdot_i4(w[u], xw);
             ta[u] = __builtin_fmaf((float)S, ps, ta[u]);
           }
         }
@@ -301,6 +318,8 @@ hipError_t launch_gemv_planes(int fmt, int xdt, bool grouped, const GemvArgs& a,
   }
   if (fmt == kFmtInt8 && !grouped)
     return xdt == kBF16 ? launch_fx<kFmtInt8, kBF16, false>(a, b, cus, st) : launch_fx<kFmtInt8, kF32, false>(a, b, cus, st);
+  if (fmt == kFmtInt3 && grouped)
+    return xdt == kBF16 ? launch_fx<kFmtInt3, kBF16, true>(a, b, cus, st) : launch_fx<kFmtInt3, kF32, true>(a, b, cus, st);
   return hipErrorNotSupported;
 }
 

@@ -56,11 +56,9 @@ constexpr size_t kDecLdsMax = 128 * 1024;   // dynamic LDS of the decode kernels
 hipError_t launch_gemv_planes(int fmt, int xdt, bool grouped, const GemvArgs& a, const GemvArgs* b, hipStream_t st);
 // compute units of the current device (cached per device, thread-safe)
 hipError_t device_cus(int* cus);
-// int3-g64 GEMV (fmt 5): y = W x for k <= kI3KMax; LDS bytes it stages.
+// int3-g64 rows (fmt 5) the kernels take: k <= kI3KMax (the expert FFN
+// stages a whole row of x or h in LDS).
 constexpr int kI3KMax = 16384;
-size_t qgemv_i3_lds(int k, int xdt);
-hipError_t launch_qgemv_i3(const uint8_t* q, const float* sc, const void* x, int xdt, float* y, int n, int k,
-                           hipStream_t st);
 // u[i] <- u[i] / sqrt(mean u^2 + eps) * g[i] in place, one workgroup.
 hipError_t launch_rmsnorm(float* u, const float* g, int n, float eps, hipStream_t st);
 
@@ -75,17 +73,6 @@ int moe_decode_tokens_per_pass(int fmt, int topk, const ExpertArgs& e);
 // from a.h first when h_from_caller)
 hipError_t launch_moe_gate_up2(int fmt, int xdt, bool grouped, const MoeDecArgs& a, hipStream_t st);
 hipError_t launch_moe_down2(int fmt, bool grouped, const MoeDecArgs& a, bool h_from_caller, hipStream_t st);
-
-// moe_int3.hip: the expert FFN for int3-g64 experts (decode kernels, any
-// number of tokens).  Shapes they take; fp32 h bytes the fused call keeps in
-// the workspace; gate+up (h = silu(G x) * (U x), fp32 [T * topk][I]) and
-// down + weighted combine (y [T][H] from that h).
-bool moe_i3_supported(int topk, const ExpertArgs& e);
-size_t moe_i3_ws_bytes(int T, int topk, const ExpertArgs& e);
-hipError_t launch_moe_i3_gate_up(int xdt, const ExpertArgs& e, const void* x, const int32_t* ids, int T, int topk,
-                                 float* h, hipStream_t st);
-hipError_t launch_moe_i3_down(const ExpertArgs& e, const float* h, const int32_t* ids, const float* w, int T,
-                              int topk, float* y, hipStream_t st);
 
 // moe_prefill.hip: the grouped MFMA path takes int4 experts whose group size
 // (or row length, per-row scales) is a multiple of 64 (grouped: a multiple of

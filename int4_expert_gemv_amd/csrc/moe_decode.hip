@@ -46,8 +46,10 @@ constexpr int kMaxPairs = 128;  // (token, slot) pairs per pass (passes are size
 
 __device__ __forceinline__ int wuni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int FMT> constexpr int per_chunk() { return FMT == kFmtInt4 ? 32 : 16; }
-template <int FMT> constexpr int x_words() { return FMT == kFmtInt4 ? 16 : 8; }  // digit words per chunk and plane
+// int3-g64 experts run as int4 (planes.hpp: the values become signed
+// nibbles when used; a 32-input chunk is 12 bytes of a 24-byte group)
+template <int FMT> constexpr int per_chunk() { return FMT == kFmtInt8 ? 16 : 32; }
+template <int FMT> constexpr int x_words() { return FMT == kFmtInt8 ? 8 : 16; }  // digit words per chunk and plane
 
 // ---- routing table ---------------------------------------------------------------
 // The valid pairs of the call grouped by expert: experts in order of first
@@ -187,12 +189,15 @@ __host__ __device__ constexpr int dn_ngp(int I) { return 8 * ((I + 127) / 128); 
 
 // element of digit j of a group's column (the weights' unpacking order: an
 // int4 word w gives bytes (w & 0x0F0F0F0F) = nibbles 0, 2, 4, 6 and
-// (w >> 4) & 0x0F0F0F0F = nibbles 1, 3, 5, 7)
+// (w >> 4) & 0x0F0F0F0F = nibbles 1, 3, 5, 7; int3 unpacks the words of its
+// even and of its odd values (i3_words) the same way)
 template <int FMT>
 __device__ __forceinline__ int dn_elem(int j) {
+  const int v = j >> 2, jj = j & 3;
   if constexpr (FMT == kFmtInt4) {
-    const int v = j >> 2, jj = j & 3;
     return ((v & 2) ? 8 : 0) + 2 * jj + (v & 1);
+  } else if constexpr (FMT == kFmtInt3) {
+    return 4 * jj + ((v & 1) ? 2 : 0) + ((v & 2) ? 1 : 0);
   } else {
     return j;
   }
@@ -252,7 +257,7 @@ __device__ __forceinline__ void wave_h_records(float v, uint8_t* __restrict__ re
     if (lane == 0) {
       int* ci = reinterpret_cast<int*>(rq + 64);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) ci[cc] = FMT == kFmtInt4 ? -8 * sum[cc] : 0;
+      for (int cc = 0; cc < 4; ++cc) ci[cc] = FMT == kFmtInt8 ? 0 : -8 * sum[cc];
       *reinterpret_cast<float*>(rq + 80) = ldexpf(1.f, E - 14 - 30 * q);
       *reinterpret_cast<int*>(rq + 84) = P;
     }
@@ -347,7 +352,14 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const uint32_t c = (uint32_t)(lane + 64 * i);
-        g.w[q][i] = ld_region16(rq, c * 16u);
+        if constexpr (FMT == kFmtInt3) {  // low words 2 (c & 1), +1 of group c / 2 and their 32 high bits
+          const uint32_t gb = (c >> 1) * 24u;
+          const u32x2 lw = __builtin_amdgcn_raw_buffer_load_b64(rq, gb + 8u * (c & 1u), 0, 2);
+          const uint32_t hw = __builtin_amdgcn_raw_buffer_load_b32(rq, gb + 16u + 4u * (c & 1u), 0, 2);
+          g.w[q][i] = u32x4{lw[0], lw[1], hw, 0u};
+        } else {
+          g.w[q][i] = ld_region16(rq, c * 16u);
+        }
         if constexpr (GROUPED) g.s[q][i] = ld_region4(rs, (c >> ex.gshift) * 4u);
       }
     }
@@ -416,7 +428,17 @@ __global__ __launch_bounds__(kGT) void moe_gu_kernel(MoeDecArgs a) {
           }
 #pragma unroll
           for (int q = 0; q < 2 * kGR; ++q) {
-            const int S = FMT == kFmtInt4 ? gdot_i4(g.w[q][i] ^ 0x88888888u, xw) : gdot_i8(g.w[q][i], xw);
+            int S;
+            if constexpr (FMT == kFmtInt4) {
+              S = gdot_i4(g.w[q][i] ^ 0x88888888u, xw);
+            } else if constexpr (FMT == kFmtInt3) {
+              uint32_t e0, o0, e1, o1;
+              i3_words(g.w[q][i][0], g.w[q][i][2] & 0xFFFFu, e0, o0);
+              i3_words(g.w[q][i][1], g.w[q][i][2] >> 16, e1, o1);
+              S = gdot_i4(u32x4{e0, o0, e1, o1}, xw);
+            } else {
+              S = gdot_i8(g.w[q][i], xw);
+            }
             ta[q] = __builtin_fmaf((float)S, ps, ta[q]);
           }
         }
@@ -601,7 +623,7 @@ constexpr int kNB = 2;                          // chunks in flight per wave
 constexpr uint32_t kOutside = 0x80000000u;      // a buffer offset past every record: loads zeros
 constexpr size_t kDnLdsMax = 144 * 1024;        // dynamic LDS of the down kernel
 
-__host__ __device__ constexpr int dn_ck2(int fmt) { return fmt == kFmtInt4 ? 4 : 2; }
+__host__ __device__ constexpr int dn_ck2(int fmt) { return fmt == kFmtInt8 ? 2 : 4; }
 // record slots per pair in LDS: whole chunks of k blocks
 __host__ __device__ constexpr int dn_ngl(int fmt, int I) {
   return 8 * dn_ck2(fmt) * (((I + 127) / 128 + dn_ck2(fmt) - 1) / dn_ck2(fmt));
@@ -629,7 +651,7 @@ template <int FMT, int SM>
 __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int xcap) {
   constexpr int CK2 = dn_ck2(FMT);
   constexpr int NS = 2 * CK2;                  // steps per chunk
-  constexpr int WV = FMT == kFmtInt4 ? 1 : 2;  // 16-byte weight loads per lane and k block
+  constexpr int WV = FMT == kFmtInt8 ? 2 : 1;  // 16-byte weight loads per lane and k block (int3: 12 bytes)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ Route R;
   __shared__ int s_xready, s_cnt[2][kMW];
@@ -700,6 +722,11 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
     if constexpr (FMT == kFmtInt4) {
       const uint32_t w0 = w[0][2 * hh], w1 = w[0][2 * hh + 1];
       return u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+    } else if constexpr (FMT == kFmtInt3) {
+      // the half's 16 values as offset-binary nibbles (signed nibble ^ 8 = value + 4), even then odd
+      uint32_t we, wo;
+      i3_words_ob(w[0][hh], (w[0][2] >> (16 * hh)) & 0xFFFFu, we, wo);
+      return u32x4{we & 0x0F0F0F0Fu, (we >> 4) & 0x0F0F0F0Fu, wo & 0x0F0F0F0Fu, (wo >> 4) & 0x0F0F0F0Fu};
     } else {
       return w[hh];
     }
@@ -787,12 +814,23 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
       rq = region_rsrc(ex.dq + er0 * ex.rb_i, ok ? (uint32_t)(rows * ex.rb_i) : 0u);
       rsc = region_rsrc(ex.ds + er0 * ex.G_i, ok ? (uint32_t)(rows * ex.G_i * 4) : 0u);
     };
-    const uint32_t qo = (uint32_t)n * (uint32_t)ex.rb_i + (FMT == kFmtInt4 ? (uint32_t)s * 16u : (uint32_t)s * 32u);
+    // lane (n, s): row n, k in [128 kb2 + 32 s, +32) -- int3: half s & 1 of
+    // group 2 kb2 + s / 2, its two low words and their 32 high bits
+    const uint32_t qo = (uint32_t)n * (uint32_t)ex.rb_i +
+                        (FMT == kFmtInt4   ? (uint32_t)s * 16u
+                         : FMT == kFmtInt3 ? (uint32_t)(s >> 1) * 24u + 8u * (uint32_t)(s & 1)
+                                           : (uint32_t)s * 32u);
     const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
     auto wload = [&](uint32_t kb2, u32x4 (&w)[WV]) __attribute__((always_inline)) {
+      if constexpr (FMT == kFmtInt3) {
+        const u32x2 lw = __builtin_amdgcn_raw_buffer_load_b64(rq, qo, 48u * kb2, 2);
+        const uint32_t hw = __builtin_amdgcn_raw_buffer_load_b32(rq, qo + 16u - 4u * (uint32_t)(s & 1), 48u * kb2, 2);
+        w[0] = u32x4{lw[0], lw[1], hw, 0u};
+      } else {
 #pragma unroll
-      for (int v = 0; v < WV; ++v)
-        w[v] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16u * v, (FMT == kFmtInt4 ? 64u : 128u) * kb2, 2);
+        for (int v = 0; v < WV; ++v)
+          w[v] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16u * v, (FMT == kFmtInt4 ? 64u : 128u) * kb2, 2);
+      }
     };
     auto load = [&](Chunk& ch) __attribute__((always_inline)) {
       if (lp == 0) task_rsrc(lt);
@@ -1114,9 +1152,9 @@ int gu_cpl(int kch) {
 // LDS bytes of the gate+up kernel: two planes of digit words and a factor per
 // chunk position, for T tokens
 size_t gu_lds(int fmt, int T, int H) {
-  const int per = fmt == kFmtInt4 ? 32 : 16;
+  const int per = fmt == kFmtInt8 ? 16 : 32;
   const size_t kchp = (size_t)64 * gu_cpl(H / per);
-  return (size_t)2 * T * kchp * (fmt == kFmtInt4 ? 16 : 8) * 4 + (size_t)T * kchp * 4;
+  return (size_t)2 * T * kchp * (fmt == kFmtInt8 ? 8 : 16) * 4 + (size_t)T * kchp * 4;
 }
 
 template <int FMT, int XT, bool GROUPED>
@@ -1202,7 +1240,7 @@ void moe_decode_ws_split(MoeDecArgs& a, void* ws) {
 
 bool moe_decode_supported(int fmt, int T, int topk, const ExpertArgs& e) {
   if (T < 1 || T * topk > kMaxPairs) return false;
-  const int per = fmt == kFmtInt4 ? 32 : 16;
+  const int per = fmt == kFmtInt8 ? 16 : 32;
   const int kh = e.H / per, ki = e.I / per;
   (void)ki;
   if (gu_cpl(kh) == 0) return false;
@@ -1217,7 +1255,7 @@ bool moe_decode_supported(int fmt, int T, int topk, const ExpertArgs& e) {
 
 // largest token count per pass whose x digit planes fit the LDS budget
 int moe_decode_tokens_per_pass(int fmt, int topk, const ExpertArgs& e) {
-  const int per = fmt == kFmtInt4 ? 32 : 16;
+  const int per = fmt == kFmtInt8 ? 16 : 32;
   if (gu_cpl(e.H / per) == 0) return 0;
   int t = (int)(kDecLdsMax / gu_lds(fmt, 1, e.H));
   t = min(t, 2 * kGT / (64 * gu_cpl(e.H / per)));  // two x groups per thread when staging
@@ -1234,6 +1272,10 @@ hipError_t launch_moe_gate_up2(int fmt, int xdt, bool grouped, const MoeDecArgs&
     if (xdt == kBF16) return grouped ? launch_gu<kFmtInt4, kBF16, true>(a, cus, st) : launch_gu<kFmtInt4, kBF16, false>(a, cus, st);
     return grouped ? launch_gu<kFmtInt4, kF32, true>(a, cus, st) : launch_gu<kFmtInt4, kF32, false>(a, cus, st);
   }
+  if (fmt == kFmtInt3) {
+    if (!grouped) return hipErrorNotSupported;
+    return xdt == kBF16 ? launch_gu<kFmtInt3, kBF16, true>(a, cus, st) : launch_gu<kFmtInt3, kF32, true>(a, cus, st);
+  }
   if (grouped) return hipErrorNotSupported;
   return xdt == kBF16 ? launch_gu<kFmtInt8, kBF16, false>(a, cus, st) : launch_gu<kFmtInt8, kF32, false>(a, cus, st);
 }
@@ -1246,6 +1288,8 @@ hipError_t launch_moe_down2(int fmt, bool grouped, const MoeDecArgs& a, bool h_f
     const int ng = a.T * a.topk * ((a.ex.I + 15) / 16);
     if (fmt == kFmtInt4)
       hipLaunchKernelGGL(h_records_kernel<kFmtInt4>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
+    else if (fmt == kFmtInt3)
+      hipLaunchKernelGGL(h_records_kernel<kFmtInt3>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
     else
       hipLaunchKernelGGL(h_records_kernel<kFmtInt8>, dim3((ng + 3) / 4), dim3(256), 0, st, a, ng);
     e = hipGetLastError();
@@ -1254,6 +1298,7 @@ hipError_t launch_moe_down2(int fmt, bool grouped, const MoeDecArgs& a, bool h_f
   // the down matrices' scale group size (0: one scale per row)
   const int gs = (grouped && a.ex.G_i > 1) ? (32 << a.ex.gshift) : 0;
   if (fmt == kFmtInt4) return launch_down<kFmtInt4>(a, gs, cus, st);
+  if (fmt == kFmtInt3) return gs == 64 ? launch_down<kFmtInt3>(a, gs, cus, st) : hipErrorNotSupported;
   if (grouped) return hipErrorNotSupported;
   return launch_down<kFmtInt8>(a, 0, cus, st);
 }

@@ -104,6 +104,41 @@ __device__ __forceinline__ void plane_words8_i4(float (&r)[8], uint32_t (&wd)[4]
   }
 }
 
+// int3-g64 weights (the colibri page "Vulkan backend: expert tier + dense +
+// MLA attention on any Vulkan 1.2 GPU", int3 commit notes: 64 inputs in 24
+// bytes, four 32-bit words of 2-bit low parts, then 64 high bits; reading:
+// value i at bits 2 (i % 16) of low word i / 16 and at bit i of the high
+// word; weight = value - 4) are the int4 case with signed nibbles:
+// w = lo + 4 hb - 4 is lo (hb = 1) or lo - 4 (hb = 0), i.e. the 4-bit two's
+// complement lo + 12 (1 - hb).  A 16-value low word gives two weight words
+// without moving any 2-bit field: its even values (lo & 0x33333333: value
+// 2k in nibble k) and its odd values ((lo >> 2) & 0x33333333), the 16 high
+// bits spread once (bit i to bit 2 i) and masked for each.  The activations
+// of those 16 inputs are staged in the same order: even ones, then odd ones.
+// bit i of the 16-bit h -> bit 2 i (so value 2k's bit lands at 4k, value
+// 2k + 1's at 4k + 2)
+__device__ __forceinline__ uint32_t spread16(uint32_t h) {
+  h = (h | (h << 8)) & 0x00FF00FFu;
+  h = (h | (h << 4)) & 0x0F0F0F0Fu;
+  h = (h | (h << 2)) & 0x33333333u;
+  return (h | (h << 1)) & 0x55555555u;
+}
+// the two signed-nibble weight words (even, odd values) of one 16-value low
+// word and its 16 high bits (bits 0..15 of h16)
+__device__ __forceinline__ void i3_words(uint32_t lo, uint32_t h16, uint32_t& we, uint32_t& wo) {
+  const uint32_t n = spread16(~h16 & 0xFFFFu);  // 1 - hb, at bit 4k (even) and 4k + 2 (odd)
+  const uint32_t ne = n & 0x11111111u, no = n & 0x44444444u;
+  we = (lo & 0x33333333u) | (ne << 2) | (ne << 3);
+  wo = ((lo >> 2) & 0x33333333u) | no | (no << 1);
+}
+// the same as offset-binary nibbles (value + 4 = signed nibble + 8, the int4
+// encoding): lo + 4 + 4 hb
+__device__ __forceinline__ void i3_words_ob(uint32_t lo, uint32_t h16, uint32_t& we, uint32_t& wo) {
+  const uint32_t b = spread16(h16 & 0xFFFFu);
+  we = (lo & 0x33333333u) + 0x44444444u + ((b & 0x11111111u) << 2);
+  wo = ((lo >> 2) & 0x33333333u) + 0x44444444u + ((b & 0x44444444u));
+}
+
 // The 2 words (low bytes, high bytes) of the current plane of 4 activations
 // (int8 weights), r advanced to the next plane.
 __device__ __forceinline__ void plane_words4_i8(float (&r)[4], uint32_t (&wd)[2]) {
@@ -210,6 +245,31 @@ __device__ __forceinline__ void load_acts(const void* __restrict__ x, int64_t e0
 template <int FMT, int XT>
 __device__ __forceinline__ void stage_group(const void* __restrict__ x, int64_t e0, int E, int p0, int np,
                                             uint32_t* __restrict__ dst, size_t pstride) {
+  if constexpr (FMT == kFmtInt3) {
+    // 32 activations as four sub-blocks of 8: the even and the odd ones of
+    // each 16 (the order of the int3 weight words, i3_words)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float v[16];
+      load_acts<XT, 16>(x, e0 + 16 * hh, v);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = ldexpf(v[2 * i + par], 14 - E);
+        skip_planes(r, p0);
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          if (pp >= np) break;
+          uint32_t wd[4];
+          plane_words8_i4(r, wd);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dst[pp * pstride + (2 * hh + par) * 4 + k] = wd[k];
+        }
+      }
+    }
+    return;
+  }
   constexpr int SB = FMT == kFmtInt4 ? 8 : 4;  // activations per sub-block
   constexpr int NSB = FMT == kFmtInt4 ? 4 : 4;  // sub-blocks per group
   constexpr int WPS = FMT == kFmtInt4 ? 4 : 2;  // words per sub-block and plane
@@ -239,21 +299,24 @@ __device__ __forceinline__ void stage_group(const void* __restrict__ x, int64_t 
 template <int FMT, int N>
 __device__ __forceinline__ void stage_group_vals(float (&v)[N], int E, int p0, uint32_t* __restrict__ dst,
                                                  size_t pstride) {
-  constexpr int SB = FMT == kFmtInt4 ? 8 : 4;
-  constexpr int WPS = FMT == kFmtInt4 ? 4 : 2;
+  constexpr int SB = FMT == kFmtInt8 ? 4 : 8;
+  constexpr int WPS = FMT == kFmtInt8 ? 2 : 4;
 #pragma unroll
   for (int j = 0; j < N / SB; ++j) {
     float r[SB];
+    // sub-block j: 8 consecutive values, or for int3 the even (j even) or
+    // odd (j odd) values of the 16 starting at 16 (j / 2)
 #pragma unroll
-    for (int i = 0; i < SB; ++i) r[i] = ldexpf(v[j * SB + i], 14 - E);
+    for (int i = 0; i < SB; ++i)
+      r[i] = ldexpf(FMT == kFmtInt3 ? v[16 * (j >> 1) + 2 * i + (j & 1)] : v[j * SB + i], 14 - E);
     skip_planes(r, p0);
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       uint32_t wd[WPS];
-      if constexpr (FMT == kFmtInt4)
-        plane_words8_i4(r, wd);
-      else
+      if constexpr (FMT == kFmtInt8)
         plane_words4_i8(r, wd);
+      else
+        plane_words8_i4(r, wd);
 #pragma unroll
       for (int k = 0; k < WPS; ++k) dst[pp * pstride + j * WPS + k] = wd[k];
     }

@@ -85,7 +85,6 @@ int check_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int6
   if (ldx < w->k || ldy < w->n) return QM_ERR_INVALID;
   if (st != QM_OK) return st;
   if (batch > QM_SMALL_MAX) return QM_ERR_UNSUPPORTED;
-  if (w->fmt == QM_FMT_INT3 && batch > 1) return QM_ERR_UNSUPPORTED;  // one token per weight read
   if (!aligned(w->q, 16) || !aligned(x, 16) || !aligned(w->scales, 4) || !aligned(y, 4))
     return QM_ERR_UNSUPPORTED;
   if ((ldx * xsize(xdt)) % 16) return QM_ERR_UNSUPPORTED;
@@ -115,11 +114,6 @@ int run_gemm(const qm_qmat* w, const void* x, int32_t xdt, int32_t batch, int64_
              void* stream) {
   int st = check_gemm(w, x, xdt, batch, ldx, y, ldy);
   if (st != QM_OK || w->n == 0) return st;
-  if (w->fmt == QM_FMT_INT3) {
-    const hipError_t e3 = launch_qgemv_i3(static_cast<const uint8_t*>(w->q), w->scales, x, xdt, y, w->n, w->k,
-                                          static_cast<hipStream_t>(stream));
-    return e3 == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
   const GemvArgs a = gemv_args(w, x, batch, ldx, y, ldy);
   const hipError_t err = launch_gemv_planes(w->fmt, xdt, eff_gs(w->fmt, w->group_size, w->k) != 0, a, nullptr,
                                             static_cast<hipStream_t>(stream));
@@ -264,7 +258,7 @@ int qgemv_pair(const qm_qmat* w1, const qm_qmat* w2, const void* x, int32_t x_dt
     return r != QM_OK ? r : run_gemm(w2, x, x_dtype, 1, w2->k, y2, w2->n, stream);
   }
   const int g1 = eff_gs(w1->fmt, w1->group_size, w1->k), g2 = eff_gs(w2->fmt, w2->group_size, w2->k);
-  if (w1->fmt == w2->fmt && (g1 != 0) == (g2 != 0) && w1->fmt != QM_FMT_INT3) {
+  if (w1->fmt == w2->fmt && (g1 != 0) == (g2 != 0)) {
     // one launch: x staged once per workgroup for both matrices
     const GemvArgs a1 = gemv_args(w1, x, 1, w1->k, y1, w1->n), a2 = gemv_args(w2, x, 1, w2->k, y2, w2->n);
     const hipError_t err = launch_gemv_planes(w1->fmt, x_dtype, g1 != 0, a1, &a2, static_cast<hipStream_t>(stream));
@@ -298,11 +292,7 @@ size_t moe_expert_ffn_workspace(const qm_experts* ex, int32_t n_tokens, int32_t 
   if (!ex || n_tokens < 0 || top_k < 1 || top_k > QM_TOPK_MAX) return 0;
   if (ex->hidden < 1 || ex->inter < 1 || ex->n_experts < 1) return 0;
   size_t need = 0;
-  if (ex->fmt == QM_FMT_INT3) {
-    // int3: the fp32 hidden vectors between the two launches
-    if (moe_shape_ok(ex) && moe_i3_supported(top_k, expert_args(ex)))
-      need = moe_i3_ws_bytes(n_tokens, top_k, expert_args(ex));
-  } else if (moe_shape_ok(ex)) {
+  if (moe_shape_ok(ex)) {
     const int tpp = dec_tokens(ex, top_k);
     if (tpp > 0) {
       const int td = n_tokens < tpp ? n_tokens : tpp;
@@ -329,18 +319,6 @@ int moe_expert_ffn_path(const qm_experts* ex, const void* x, int32_t x_dtype, in
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
-  if (ex->fmt == QM_FMT_INT3) {  // decode kernels only, any number of tokens
-    const ExpertArgs e = expert_args(ex);
-    if (path == QM_PATH_PREFILL || !moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
-      return QM_ERR_WORKSPACE;
-    float* h = static_cast<float*>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = launch_moe_i3_gate_up(x_dtype, e, x, topk_ids, n_tokens, top_k, h, s);
-    if (err == hipSuccess) err = launch_moe_i3_down(e, h, topk_ids, topk_w, n_tokens, top_k, y, s);
-    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
-    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
@@ -383,16 +361,6 @@ int moe_gate_up(const qm_experts* ex, const void* x, int32_t x_dtype, int32_t n_
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(h, 4) || !aligned(topk_ids, 4)) return QM_ERR_UNSUPPORTED;
-  if (ex->fmt == QM_FMT_INT3) {
-    const ExpertArgs e = expert_args(ex);
-    if (!moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
-      return QM_ERR_WORKSPACE;
-    const hipError_t err =
-        launch_moe_i3_gate_up(x_dtype, e, x, topk_ids, n_tokens, top_k, h, static_cast<hipStream_t>(stream));
-    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
-    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;
@@ -422,16 +390,6 @@ int moe_down(const qm_experts* ex, const float* h, int32_t n_tokens, const int32
   if (st != QM_OK) return st;
   if (top_k > QM_TOPK_MAX) return QM_ERR_UNSUPPORTED;
   if (!aligned(h, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QM_ERR_UNSUPPORTED;
-  if (ex->fmt == QM_FMT_INT3) {
-    const ExpertArgs e = expert_args(ex);
-    if (!moe_i3_supported(top_k, e)) return QM_ERR_UNSUPPORTED;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < moe_expert_ffn_workspace(ex, n_tokens, top_k))
-      return QM_ERR_WORKSPACE;
-    const hipError_t err =
-        launch_moe_i3_down(e, h, topk_ids, topk_w, n_tokens, top_k, y, static_cast<hipStream_t>(stream));
-    if (err == hipErrorNotSupported) return QM_ERR_UNSUPPORTED;
-    return err == hipSuccess ? QM_OK : QM_ERR_LAUNCH;
-  }
   bool grouped = false;
   st = moe_grouping(ex, &grouped);
   if (st != QM_OK) return st;

@@ -132,9 +132,8 @@ def test_qgemv_norm_chain_rejects(q):
 
 
 def test_int3_limits(q):
-    """int3-g64: group size 64 only, k <= 16384, one token per weight read;
-    as an expert format, decode kernels only (no prefill path) and the
-    top-k hidden vectors of a token must fit one workgroup's LDS."""
+    """int3-g64: group size 64 only, k <= 16384, batches as for int4;
+    as an expert format, the decode kernels' limits (no prefill path)."""
     f = ctypes.c_void_p(FAKE)
     st = lambda m: q.raw_status("qgemv", ctypes.byref(m), f, 1, f, None)
     assert st(_mat(q, fmt=5, gs=0)) == -1                  # int3 needs group size 64
@@ -142,15 +141,15 @@ def test_int3_limits(q):
     assert st(_mat(q, fmt=5, k=16416)) == -2               # k above the staged maximum
     assert st(_mat(q, fmt=5, k=80)) == -2                  # k not a multiple of 32
     m = _mat(q, fmt=5)
-    assert q.raw_status("qgemm_small", ctypes.byref(m), f, 1, 2, ctypes.c_int64(512), f, ctypes.c_int64(64),
-                        None) == -2                        # batch > 1
+    assert q.raw_status("qgemm_small", ctypes.byref(m), f, 1, 9, ctypes.c_int64(512), f, ctypes.c_int64(64),
+                        None) == -2                        # batch above QM_SMALL_MAX
     assert _moe(q, _experts(q, fmt=5, gs=0)) == -1         # group size 64 only
     assert _moe(q, _experts(q, fmt=5, gs=64), path=2) == -2  # no prefill kernels for int3
-    assert _moe(q, _experts(q, fmt=5, gs=64, I=16384), k=32) == -2  # 32 x 16384 hidden values per token
+    assert _moe(q, _experts(q, fmt=5, gs=64, I=16384), k=32) == -2  # inter past the down kernel's limit
     assert _moe(q, _experts(q, fmt=5, gs=64, H=16416)) == -2
-    assert _moe(q, _experts(q, fmt=5, gs=64), ws_bytes=16) == -3  # workspace below T * k * inter floats
+    assert _moe(q, _experts(q, fmt=5, gs=64), ws_bytes=16) == -3  # workspace too small
     ex = _experts(q, fmt=5, gs=64)
-    assert q.moe_expert_ffn_workspace(ex, 3, 8) == 3 * 8 * 128 * 4
+    assert q.moe_expert_ffn_workspace(ex, 3, 8) >= 3 * 8 * 128 * 4  # at least h's records for every pair
 
 
 def test_qgemm_small_rejects(q):

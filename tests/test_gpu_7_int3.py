@@ -1,8 +1,10 @@
 """GPU parity of the int3-g64 two-plane GEMV (fmt 5) against the fp64
 oracle: dense decode shapes, fp32 and bf16 activations, ragged rows, a
-ragged tail group (k not a multiple of 64), the largest k, the pair entry
-point, and bit-exact results on integer-valued data with power-of-two
-scales (every partial sum exact in fp32, so any decode slip shows).
+ragged tail group (k not a multiple of 64), the largest k, several
+activation rows per weight read, the pair entry point, and bit-exact
+results on integer-valued data with power-of-two scales (every partial sum
+exact in fp32, so any decode slip shows).  Activations with an outlier on a
+zero weight are in test_gpu_8_outliers.py.
 Bar: max normalised error <= 2e-4.
 """
 import numpy as np
@@ -57,6 +59,21 @@ def test_int3_exact_integer_data(q, oracle, xdt):
     y = _run(q, n, k, qw, s, x)
     yr, _ = oracle.gemv(5, n, k, 64, qw, s, x)
     assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("batch,xdt", [(2, "bf16"), (5, "f32"), (8, "bf16")])
+def test_int3_qgemm_small(q, oracle, batch, xdt):
+    """Several activation rows per weight read."""
+    n, k = 1000, 6144
+    g = np.random.default_rng([34, batch])
+    qw, s = synth.quant_matrix(g, 5, n, k, 64)
+    x = synth.activations(g, (batch, k), xdt)
+    m = q.qmat(5, dev(qw), dev(s), n, k, 64)
+    y = torch.full((batch, n), float("nan"), device="cuda")
+    q.qgemm_small(m, dev(x), y)
+    torch.cuda.synchronize()
+    yr, nr = oracle.gemm_small(5, n, k, 64, qw, s, x)
+    assert norm_err(host(y), yr, nr) <= TOL
 
 
 def test_int3_pair(q, oracle):

@@ -9,7 +9,7 @@ error it causes would.  A kernel that rounds each activation relative to
 the largest one near it fails this; one whose error is relative to each
 activation itself passes.  The same construction is applied to the hidden
 vector of the down projection (caller-supplied h) and to x of the whole
-expert layer (zero gate and up columns).
+expert layer (zero gate and up columns), for int4, int8 and int3 weights.
 """
 import numpy as np
 import pytest
@@ -45,8 +45,19 @@ def as_dtype(x, xdt):
 
 
 def zero_column(fmt, qw, col):
-    """Set element `col` of every row to the zero weight (nibble 8 / int8 0)."""
+    """Set element `col` of every row to the zero weight (nibble 8 / int8 0 /
+    int3 value 4: low part 0, high bit 1)."""
     qw = qw.copy()
+    if fmt == 5:
+        g, i = col // 64, col % 64
+        b = np.ascontiguousarray(qw[:, 24 * g:24 * g + 24])
+        lo = np.ascontiguousarray(b[:, :16]).view("<u4")
+        hi = np.ascontiguousarray(b[:, 16:]).view("<u8")
+        lo[:, i // 16] &= np.uint32(~(3 << (2 * (i % 16))) & 0xFFFFFFFF)
+        hi[:, 0] |= np.uint64(1) << np.uint64(i)
+        qw[:, 24 * g:24 * g + 16] = lo.view(np.uint8)
+        qw[:, 24 * g + 16:24 * g + 24] = hi.view(np.uint8)
+        return qw
     if fmt == 4:
         b = qw[:, col // 2]
         qw[:, col // 2] = (b & 0xF0) | 8 if col % 2 == 0 else (b & 0x0F) | 0x80
@@ -59,6 +70,7 @@ GEMV_SHAPES = [
     (4, 512, 6144, 64, "bf16"), (4, 300, 16384, 0, "f32"), (4, 256, 2048, 32, "bf16"),
     (1, 512, 6144, 0, "bf16"), (1, 300, 2048, 0, "f32"),
     (4, 256, 512, 64, "f32"), (4, 77, 96, 0, "bf16"), (1, 19, 48, 0, "bf16"),
+    (5, 512, 6144, 64, "bf16"), (5, 300, 16384, 64, "f32"), (5, 77, 96, 64, "bf16"), (5, 256, 2048, 64, "bf16"),
 ]
 
 
@@ -95,7 +107,7 @@ def test_qgemv_extreme_fp32_outlier(q, oracle, ratio):
     assert norm_err(host(y), yr, nr) <= TOL
 
 
-@pytest.mark.parametrize("fmt,gs", [(4, 64), (1, 0)])
+@pytest.mark.parametrize("fmt,gs", [(4, 64), (1, 0), (5, 64)])
 @pytest.mark.parametrize("ratio", RATIOS)
 def test_qgemv_pair_outlier(q, oracle, fmt, gs, ratio):
     k, n1, n2 = 6144, 2048, 576
@@ -114,7 +126,8 @@ def test_qgemv_pair_outlier(q, oracle, fmt, gs, ratio):
         assert norm_err(host(y), yr, nr) <= TOL
 
 
-@pytest.mark.parametrize("fmt,gs,xdt,batch", [(4, 64, "bf16", 2), (4, 64, "f32", 8), (1, 0, "bf16", 4)])
+@pytest.mark.parametrize("fmt,gs,xdt,batch", [(4, 64, "bf16", 2), (4, 64, "f32", 8), (1, 0, "bf16", 4),
+                                              (5, 64, "bf16", 3)])
 @pytest.mark.parametrize("ratio", (2.0 ** 12, 2.0 ** 24))
 def test_qgemm_small_outlier(q, oracle, fmt, gs, xdt, batch, ratio):
     n, k = 1024, 6144
@@ -152,6 +165,7 @@ def _qexperts(q, ex):
 @pytest.mark.parametrize("fmt,gs,E,H,I,T", [
     (4, 64, 16, 6144, 2048, 1), (4, 64, 16, 6144, 2048, 3), (4, 0, 16, 6144, 2048, 1),
     (4, 64, 32, 2048, 512, 1), (1, 0, 8, 1024, 512, 2), (4, 64, 12, 1024, 256, 5),
+    (5, 64, 16, 6144, 2048, 1), (5, 64, 32, 2048, 512, 3),
 ])
 @pytest.mark.parametrize("ratio", RATIOS)
 def test_moe_down_outlier_h(q, oracle, fmt, gs, E, H, I, T, ratio):
@@ -188,6 +202,7 @@ def _silu(z):
 
 @pytest.mark.parametrize("fmt,gs,E,H,I,T", [
     (4, 64, 16, 6144, 2048, 1), (4, 64, 32, 2048, 512, 1), (4, 0, 16, 6144, 2048, 2), (1, 0, 8, 1024, 512, 1),
+    (5, 64, 16, 6144, 2048, 1), (5, 64, 32, 2048, 512, 2),
 ])
 @pytest.mark.parametrize("ratio", RATIOS)
 def test_moe_gate_up_outlier_x(q, oracle, fmt, gs, E, H, I, T, ratio):
@@ -224,6 +239,8 @@ def test_moe_gate_up_outlier_x(q, oracle, fmt, gs, E, H, I, T, ratio):
     (4, 0, 24, 6144, 2048, 1),
     (4, 64, 24, 6144, 2048, 4),
     (1, 0, 8, 1024, 512, 2),
+    (5, 64, 24, 6144, 2048, 1),    # int3-g64 experts
+    (5, 64, 64, 2048, 512, 2),
 ])
 @pytest.mark.parametrize("ratio", RATIOS)
 def test_moe_layer_outlier_x(q, oracle, fmt, gs, E, H, I, T, ratio):
