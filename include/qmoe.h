@@ -50,15 +50,17 @@
  *    order: value i of a group at bits 2 (i % 16) of little-endian low word
  *    i / 16 and at bit i of the little-endian high word; element = value - 4.
  *    Rows are ceil(k/64) * 24 bytes (a ragged last group is padded).
- *    group_size must be 64.  qgemv, qgemv_pair and qgemm_small with batch 1
- *    take it (k <= 16384).  The expert FFN takes it through its decode
- *    kernels for any number of tokens (hidden, inter <= 16384 and multiples
- *    of 32; top_k * ceil(inter / 64) <= 512); it has no prefill kernels
- *    (QM_PATH_PREFILL gives QM_ERR_UNSUPPORTED) [V: int3 commit notes, int3
- *    expert matmuls and fused gate_up].
+ *    group_size must be 64; k a multiple of 32, k <= 16384.  qgemv,
+ *    qgemv_pair, qgemm_small (any batch) and the expert FFN take it: the
+ *    kernels are the int4 ones, each value turned into a signed nibble
+ *    (element = lo + 4 hb - 4) as it is loaded, so int3 has the int4
+ *    arithmetic and limits.  The expert FFN runs it on its decode kernels
+ *    for any number of tokens; it has no prefill kernels (QM_PATH_PREFILL
+ *    gives QM_ERR_UNSUPPORTED) [V: int3 commit notes, int3 expert matmuls
+ *    and fused gate_up].
  *  Value = element * its scale.
  *
- * Arithmetic.  The int4 and int8 kernels apply the weights with integer dot
+ * Arithmetic.  The int4, int3 and int8 kernels apply the weights with integer dot
  * products (eight int4 or four int8 products per instruction) to activations
  * written as stacked 15-bit integer "digit planes": each group of 32 (int4) or
  * 16 (int8) activations shares a power-of-two exponent, and a call uses as
@@ -67,9 +69,9 @@
  * fp32 hidden vector, in groups of 16).  The error of an output is therefore
  * at most 2^-15 * sum_k |w_k x_k| plus fp32 accumulation, for any finite
  * input: a large activation beside small ones costs more planes (more
- * work), not accuracy.  Typical activations need two planes.  The int3
- * GEMV (QM_FMT_INT3) and the prefill kernels (bf16 MFMA) use floating-point
- * products instead (see their entry points).
+ * work), not accuracy.  Typical activations need two planes.  The prefill
+ * kernels (bf16 MFMA) use floating-point products instead (see
+ * moe_expert_ffn).
  *
  * Shape limits of the GPU path (QM_ERR_UNSUPPORTED otherwise): int4 needs
  * k % 32 == 0, int8 needs k % 16 == 0; 1 <= k <= QM_K_MAX; q and x must be
@@ -165,7 +167,7 @@ QM_API int qgemv_norm_chain(const qm_qmat *w_a, const qm_qmat *w_kv, const float
                             void *stream);
 
 /* Y[t][r] = sum_c W[r][c] * X[t][c] for t < batch, reading W once for all
- * t (int4 and int8; int3 takes batch 1 only).
+ * t (int4, int3 and int8).
  * [V: qmatmul.comp note -- the S-token batch of the same GEMV]
  * x: device [batch][ldx] (ldx >= k, ldx*elemsize a multiple of 16 bytes).
  * y: device [batch][ldy] fp32 (ldy >= n).  1 <= batch <= QM_SMALL_MAX.     */
@@ -204,9 +206,8 @@ QM_API size_t moe_expert_ffn_workspace(const qm_experts *ex, int32_t n_tokens, i
  * arrays), hidden % 512 == 0, inter % 256 == 0, n_experts <= 8192 -- and
  * otherwise the decode kernels pass by pass.  The decode kernels take
  * hidden up to 16384 (int4; 8192 int8) and inter up to 4096 (int4; 2048
- * int8); other shapes return QM_ERR_UNSUPPORTED.  int3-g64 experts run
- * their own decode kernels for any n_tokens (each token's routed pairs read
- * their expert rows; no union of experts across tokens).                  */
+ * int8; int3 as int4); other shapes return QM_ERR_UNSUPPORTED.  int3-g64
+ * experts always run the decode kernels (pass by pass for large batches).  */
 QM_API int moe_expert_ffn(const qm_experts *ex, const void *x, int32_t x_dtype, int32_t n_tokens,
                    const int32_t *topk_ids, const float *topk_w, int32_t top_k,
                    float *y, void *workspace, size_t workspace_bytes, void *stream);

@@ -56,8 +56,8 @@ constexpr size_t kDecLdsMax = 128 * 1024;   // dynamic LDS of the decode kernels
 hipError_t launch_gemv_planes(int fmt, int xdt, bool grouped, const GemvArgs& a, const GemvArgs* b, hipStream_t st);
 // compute units of the current device (cached per device, thread-safe)
 hipError_t device_cus(int* cus);
-// int3-g64 rows (fmt 5) the kernels take: k <= kI3KMax (the expert FFN
-// stages a whole row of x or h in LDS).
+// int3-g64 rows (fmt 5) the library takes: k <= kI3KMax (the int4 kernels
+// run them; this is the range the int3 parity tests cover).
 constexpr int kI3KMax = 16384;
 // u[i] <- u[i] / sqrt(mean u^2 + eps) * g[i] in place, one workgroup.
 hipError_t launch_rmsnorm(float* u, const float* g, int n, float eps, hipStream_t st);

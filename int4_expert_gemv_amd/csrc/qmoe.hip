@@ -40,7 +40,7 @@ int eff_gs(int fmt, int gs, int k) {
 // Shape checks for one n x k matrix in (fmt, gs).  Returns a qm_status.
 int check_shape(int fmt, int n, int k, int gs) {
   if (fmt != QM_FMT_INT4 && fmt != QM_FMT_INT8_ROW && fmt != QM_FMT_INT3) return QM_ERR_INVALID;
-  if (fmt == QM_FMT_INT3) {  // int3-g64: group size 64 only, rows staged whole
+  if (fmt == QM_FMT_INT3) {  // int3-g64: group size 64 only
     if (n < 0 || k < 0 || gs != 64) return QM_ERR_INVALID;
     if (k == 0 || k > kI3KMax || k % 32) return QM_ERR_UNSUPPORTED;
     return QM_OK;
