@@ -821,15 +821,17 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
                          : FMT == kFmtInt3 ? (uint32_t)(s >> 1) * 24u + 8u * (uint32_t)(s & 1)
                                            : (uint32_t)s * 32u);
     const uint32_t so = (uint32_t)n * (uint32_t)ex.G_i * 4u;
+    // (cached loads: the 16 rows x 64 bytes of one k block are half of each
+    // row's 128-byte line, whose other half the next k block reads at once)
     auto wload = [&](uint32_t kb2, u32x4 (&w)[WV]) __attribute__((always_inline)) {
       if constexpr (FMT == kFmtInt3) {
-        const u32x2 lw = __builtin_amdgcn_raw_buffer_load_b64(rq, qo, 48u * kb2, 2);
-        const uint32_t hw = __builtin_amdgcn_raw_buffer_load_b32(rq, qo + 16u - 4u * (uint32_t)(s & 1), 48u * kb2, 2);
+        const u32x2 lw = __builtin_amdgcn_raw_buffer_load_b64(rq, qo, 48u * kb2, 0);
+        const uint32_t hw = __builtin_amdgcn_raw_buffer_load_b32(rq, qo + 16u - 4u * (uint32_t)(s & 1), 48u * kb2, 0);
         w[0] = u32x4{lw[0], lw[1], hw, 0u};
       } else {
 #pragma unroll
         for (int v = 0; v < WV; ++v)
-          w[v] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16u * v, (FMT == kFmtInt4 ? 64u : 128u) * kb2, 2);
+          w[v] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16u * v, (FMT == kFmtInt4 ? 64u : 128u) * kb2, 0);
       }
     };
     auto load = [&](Chunk& ch) __attribute__((always_inline)) {
@@ -846,7 +848,7 @@ __global__ __launch_bounds__(kMT) void moe_down_kernel(MoeDecArgs a, int PR, int
                 // in its words 0 and 2
 #pragma unroll
         for (int v = 0; v < (CK2 + 1) / 2; ++v)
-          ch.sc4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsc, so + (uint32_t)(s >> 1) * 4u, (uint32_t)(2 * k0 + 4 * v) * 4u, 2);
+          ch.sc4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsc, so + (uint32_t)(s >> 1) * 4u, (uint32_t)(2 * k0 + 4 * v) * 4u, 0);
       }
 #pragma unroll
       for (int kk = 0; kk < CK2; ++kk) wload((uint32_t)(k0 + kk), ch.w[kk]);
