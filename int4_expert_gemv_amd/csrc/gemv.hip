@@ -7,7 +7,8 @@
 // row, and int3-g64 (the int3 commit notes of the same page; as signed
 // nibbles, planes.hpp), on the activation digit planes of planes.hpp.
 //
-// Work split.  A persistent grid of about one workgroup (eight waves) per CU.
+// Work split.  A persistent grid of as many workgroups (eight waves each) as
+// the CUs hold at once (one or two per CU, by the kernel's registers).
 // A row's inputs are cut into chunks of 32 int4 (16 bytes), 16 int8 (16
 // bytes) or 32 int3 weights (12 bytes: half a 24-byte group -- two low-part
 // words and their 32 high bits -- turned into four signed-nibble words when
@@ -244,9 +245,25 @@ hipError_t launch_cpl(const GemvArgs& a, const GemvArgs* b, int cus, hipStream_t
   constexpr int NU = NB == 1 ? (CPL <= 2 ? 4 : (CPL <= 4 ? 2 : 1)) : (NB == 2 && CPL <= 2 ? 2 : 1);
   const int nrows = a.n + (b ? b->n : 0);
   const int ntiles = (nrows + NU - 1) / NU;
-  int blocks = (ntiles + kGvWaves - 1) / kGvWaves;
-  if (blocks > cus) blocks = cus;
   constexpr size_t lds = gv_lds<FMT, NB, CPL>();
+  const void* f = reinterpret_cast<const void*>(&gemv_kernel<FMT, XT, NB, CPL, NU, GROUPED>);
+  // as many workgroups as the compute units hold at once (two per CU for the
+  // kernels with few registers, e.g. int8 rows of 6144: more loads in
+  // flight; one for the others, whose extra workgroups would only queue);
+  // looked up once per kernel (racing first calls store the same value)
+  static std::atomic<int> per_cu{0};
+  int occ = per_cu.load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, kGvThreads, lds) != hipSuccess || occ < 1) {
+      (void)hipGetLastError();
+      occ = 1;
+    }
+    occ = occ > 2 ? 2 : occ;
+    per_cu.store(occ, std::memory_order_relaxed);
+  }
+  int blocks = (ntiles + kGvWaves - 1) / kGvWaves;
+  if (blocks > occ * cus) blocks = occ * cus;
   hipLaunchKernelGGL((gemv_kernel<FMT, XT, NB, CPL, NU, GROUPED>), dim3(blocks), dim3(kGvThreads), lds, st, a,
                      b ? *b : a, b ? b->n : 0);
   return hipGetLastError();
