@@ -241,8 +241,10 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
 
 template <int FMT, int XT, int NB, int CPL, bool GROUPED>
 hipError_t launch_cpl(const GemvArgs& a, const GemvArgs* b, int cus, hipStream_t st) {
-  // rows per tile: enough registers for two tiles of weights
-  constexpr int NU = NB == 1 ? (CPL <= 2 ? 4 : (CPL <= 4 ? 2 : 1)) : (NB == 2 && CPL <= 2 ? 2 : 1);
+  // rows per tile: enough registers for two tiles of weights; grouped rows
+  // of 3-4 chunks per lane take one row per tile, which leaves room for two
+  // workgroups per CU (measured faster than two rows and one workgroup)
+  constexpr int NU = NB == 1 ? (CPL <= 2 ? 4 : (CPL <= 4 ? (GROUPED ? 1 : 2) : 1)) : (NB == 2 && CPL <= 2 ? 2 : 1);
   const int nrows = a.n + (b ? b->n : 0);
   const int ntiles = (nrows + NU - 1) / NU;
   constexpr size_t lds = gv_lds<FMT, NB, CPL>();
