@@ -243,8 +243,13 @@ template <int FMT, int XT, int NB, int CPL, bool GROUPED>
 hipError_t launch_cpl(const GemvArgs& a, const GemvArgs* b, int cus, hipStream_t st) {
   // rows per tile: enough registers for two tiles of weights; grouped rows
   // of 3-4 chunks per lane take one row per tile, which leaves room for two
-  // workgroups per CU (measured faster than two rows and one workgroup)
-  constexpr int NU = NB == 1 ? (CPL <= 2 ? 4 : (CPL <= 4 ? (GROUPED ? 1 : 2) : 1)) : (NB == 2 && CPL <= 2 ? 2 : 1);
+  // workgroups per CU (measured faster than two rows and one workgroup);
+  // 4-bit weights at batch 8 take two rows, which share each read of the
+  // activation digits (int8 rows measured slower so)
+  constexpr int NU = NB == 1   ? (CPL <= 2 ? 4 : (CPL <= 4 ? (GROUPED ? 1 : 2) : 1))
+                     : NB == 2 ? (CPL <= 2 ? 2 : 1)
+                     : NB == 8 ? (CPL <= 2 && FMT != kFmtInt8 ? 2 : 1)
+                               : 1;
   const int nrows = a.n + (b ? b->n : 0);
   const int ntiles = (nrows + NU - 1) / NU;
   constexpr size_t lds = gv_lds<FMT, NB, CPL>();

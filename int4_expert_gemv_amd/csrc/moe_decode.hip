@@ -128,15 +128,8 @@ __device__ void build_route(int id_t, float w_t, int np, int E, Route& R) {
   __syncthreads();
 }
 
-// Reductions over aligned groups of G (4, 8 or 16) lanes with DPP row
+// Min or max over aligned groups of G (4, 8 or 16) lanes with DPP row
 // operations; every lane of a group ends with the result.
-template <int G>
-__device__ __forceinline__ uint32_t group_or(uint32_t v) {
-  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // lane ^ 1
-  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // lane ^ 2
-  if constexpr (G >= 8) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // other quad
-  return v;
-}
 template <int G, bool MAX>
 __device__ __forceinline__ float group_minmax(float v) {
   auto step = [&](float a, float b) __attribute__((always_inline)) { return MAX ? fmaxf(a, b) : fminf(a, b); };

@@ -178,15 +178,6 @@ __device__ __forceinline__ int gdot_i4(const u32x4& w, const uint32_t* x) {
   return t;
 }
 
-// Exact integer sum over 16 int4 weights (words w0, w1, each XOR
-// 0x88888888) against one plane of their 16-group (x[0..7]: words 4j + d).
-__device__ __forceinline__ int gdot16_i4(uint32_t w0, uint32_t w1, const uint32_t* x) {
-  int t = sdot8(w1, x[4 + 3], sdot8(w0, x[3], 0));
-#pragma unroll
-  for (int d = 2; d >= 0; --d) t = sdot8(w1, x[4 + d], sdot8(w0, x[d], shl4(t)));
-  return t;
-}
-
 // The same for 16 int8 weights (words w[0..3]) against a 16-group's plane.
 __device__ __forceinline__ int gdot_i8(const u32x4& w, const uint32_t* x) {
   int t = sdot4(w[0], x[1], sdot4(w[1], x[3], sdot4(w[2], x[5], sdot4(w[3], x[7], 0))));
