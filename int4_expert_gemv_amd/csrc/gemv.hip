@@ -16,11 +16,11 @@
 // lane l takes chunks l + 64 i of every row.  The reduction runs over
 // segments of 64 * CPL chunks (one segment covers a row when the digit planes
 // of all its activations fit the LDS budget).  Per segment the workgroup
-// first issues its first row tiles' weight loads, then turns the segment's
-// activations into digit planes in LDS -- once per workgroup, for all its
-// rows -- and then every wave walks its row tiles (NU rows; tiles
-// wave, wave + all waves, ...) with the next tile's weights loaded into a
-// second register buffer while the current one is computed.  A plane's
+// turns the segment's activations into digit planes in LDS -- once per
+// workgroup, for all its rows; their loads go first, so that they do not
+// wait behind weight requests -- and then every wave walks its row tiles
+// (NU rows; tiles wave, wave + all waves, ...) with the next tile's weights
+// loaded into a second register buffer while the current one is computed.  A plane's
 // digits are read from LDS once per chunk for all NU rows of the tile.  The
 // rows of a second matrix of the same x (qgemv_pair) continue the row index
 // space of the first.  Per-lane partial sums are reduced across the wave in
@@ -185,9 +185,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
 
   for (int seg = 0; seg < nseg; ++seg) {
     const int c0 = seg * SEGC;
-    // 1. the first tile's weights in flight before the staging work
-    if (w0 < ntiles) load_tile(wa, sa, w0, c0);
-    // 2. the segment's activations as digit planes in LDS (all planes the
+    // 1. the segment's activations as digit planes in LDS (all planes the
     //    segment needs; the plane count is the largest over its groups)
     if (seg > 0) __syncthreads();  // every wave is done with the previous segment's planes
     if (threadIdx.x == 0) *pslot = 0;
@@ -223,10 +221,11 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GemvArgs a0, GemvArgs 
         }
       }
       __syncthreads();
-      // 3. the wave's tiles, the next one's weights loading while one is computed
+      // 2. the wave's tiles (the first one's weights requested now), the next
+      //    one's weights loading while one is computed
       const bool first = seg == 0 && p0 == 0;
       int tile = w0;
-      if (p0 > 0 && tile < ntiles) load_tile(wa, sa, tile, c0);
+      if (tile < ntiles) load_tile(wa, sa, tile, c0);
       for (; tile < ntiles; tile += 2 * wstep) {
         const int t1 = tile + wstep, t2 = tile + 2 * wstep;
         if (t1 < ntiles) load_tile(wb, sb, t1, c0);
