@@ -53,8 +53,8 @@ template <int FMT> constexpr int x_words() { return FMT == kFmtInt8 ? 8 : 16; } 
 
 // ---- routing table ---------------------------------------------------------------
 // The valid pairs of the call grouped by expert: experts in order of first
-// appearance, each expert's pairs in pair order.  Built by the whole
-// workgroup in LDS.
+// appearance, each expert's pairs in pair order.  Built in LDS (by one wave
+// for up to 64 pairs, else by the whole workgroup).
 struct Route {
   int np, nu;                   // pairs, unique experts
   int uexp[kMaxPairs];          // expert id of unique u
@@ -72,6 +72,58 @@ struct Route {
 // loaded by the caller, so that other loads can be in flight meanwhile)
 __device__ void build_route(int id_t, float w_t, int np, int E, Route& R) {
   const int tid = threadIdx.x;
+  if (np <= 64) {
+    // up to 64 pairs: wave 0 builds the table in registers (lane j = pair
+    // j), one barrier publishes it
+    if (tid < 64) {
+      const int lane = tid;
+      const bool in = lane < np;
+      const int id = in ? id_t : -1;
+      const bool valid = in && id >= 0 && id < E;
+      // first pair with this expert, pairs before this one with it, and all
+      // pairs with it
+      int first = valid ? lane : -1, rank = 0, total = 0;
+      for (int i = 0; i < np; ++i) {
+        const int xi = __builtin_amdgcn_readlane(id, i);
+        if (valid && xi == id) {
+          first = min(first, i);
+          rank += i < lane ? 1 : 0;
+          ++total;
+        }
+      }
+      const bool is_first = valid && first == lane;
+      const unsigned long long fm = __ballot(is_first);
+      const int u = __popcll(fm & ((1ull << lane) - 1));  // unique index of a first pair
+      // pair offsets of the experts: exclusive prefix of the first pairs' counts
+      const int v = is_first ? total : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int start = __shfl(incl - v, valid ? first : 0, 64);
+      if (in) {
+        R.tmp_id[lane] = id_t;
+        R.wgt[lane] = w_t;
+        R.tmp_first[lane] = valid ? first : -1;
+      }
+      if (is_first) {
+        R.uexp[u] = id;
+        R.ustart[u] = incl - v;
+      }
+      if (valid) R.upair[start + rank] = lane;
+      const int nvalid = __shfl(incl, 63, 64);
+      if (lane == 0) {
+        const int nu = __popcll(fm);
+        R.nu = nu;
+        R.np = np;
+        R.ustart[nu] = nvalid;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   if (tid < np) {
     R.tmp_id[tid] = id_t;
     R.wgt[tid] = w_t;
